@@ -1,0 +1,207 @@
+"""Benchmark of the frozen MoE expert grouped GEMM (forward FC1 -> SwiGLU -> FC2
+plus the input gradient) on one MI355X.
+
+One step = gg_forward_fc1_swiglu (saving H1) + gg_forward_fc2 + gg_dgrad
+over one synthetic batch that is already resident in HBM.  Prints ONE JSON
+line: grouped-GEMM TFLOP/s (12*M*H*F per step), routed rows/s, tokens/s,
+the roofline record of the dominant kernel (MFMA-bound FC1 grouped GEMM,
+timed with HIP events on the launch stream) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped-GEMM TFLOP/s + routed tokens/s (fwd+dgrad), % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+DEFAULT_WORKLOAD = "uniform_e32_h2048_f768"
+KERNEL_SOURCES = ["moe_expert_grouped_ragged_amd/csrc/gg_kernels.hip",
+                  "moe_expert_grouped_ragged_amd/csrc/gg_kernels.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(M, H, F, n_live):
+    """Forward and dgrad algorithmic HBM bytes (weights of non-empty experts
+    read once per pass; activations read/written once)."""
+    w_act = 6 * H * F * n_live
+    fwd = w_act + 4 * M * H + 8 * M * F
+    dgrad = w_act + 4 * M * H + 12 * M * F
+    return fwd, dgrad
+
+
+def load_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    stored in profiles/traffic.json; null when the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload_name, {}).get(kernel)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, target_s: float):
+    """The CPU oracle, as it stands, on the first k rows of every non-empty
+    expert (k calibrated to about target_s seconds of work)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    w1 = oracle._as_f32(case.w1)
+    w2 = oracle._as_f32(case.w2)
+    off = case.offsets
+    live = [e for e in range(case.E) if off[e + 1] > off[e]]
+
+    def run(k):
+        rows = np.concatenate([np.arange(off[e], min(off[e] + k, off[e + 1])) for e in live]).astype(np.int64)
+        _, comp = oracle.sample_rows(off, rows)
+        xs = case.x[torch.from_numpy(rows)]
+        dys = case.dy[torch.from_numpy(rows)]
+        t0 = time.perf_counter()
+        fw = oracle.forward(xs, comp, w1, w2)
+        oracle.dgrad(dys, fw["h1"], comp, w1, w2)
+        return rows.size, time.perf_counter() - t0
+
+    n, t = run(4)
+    per_row = t / max(n, 1)
+    k = max(4, int(target_s / max(per_row * len(live), 1e-9)))
+    n, t = run(k)
+    flops = 12.0 * n * case.H * case.F
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {k} rows of each of the {len(live)} non-empty experts ({n} routed rows "
+                      f"of {case.M}), forward + dgrad, {t:.1f} s",
+            "rows_per_s": n / t, "seconds": t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (no sharding or collectives are part of it); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workload
+    import moe_expert_grouped_ragged_amd as gg
+
+    w = workload.by_name(args.workload)
+    case = workload.draw_case(w)
+    E, H, F, M = case.E, case.H, case.F, case.M
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, dy = case.x.to(dev), case.dy.to(dev)
+    off = torch.from_numpy(case.offsets).to(dev)
+    packed = gg.gg_pack_weights(case.w1.to(dev), case.w2.to(dev))
+    h1 = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
+    a = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    ev = {k: [] for k in ("fc1", "fc2", "dgrad")}
+
+    def step(record):
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            e3 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
+        if record:
+            e1.record(stream)
+        gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
+        if record:
+            e2.record(stream)
+        gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
+        if record:
+            e3.record(stream)
+            ev["fc1"].append((e0, e1))
+            ev["fc2"].append((e1, e2))
+            ev["dgrad"].append((e2, e3))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    call_ms = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in ev.items()}
+
+    flops = workload.flops_fwd_dgrad(M, H, F)
+    tflops = flops / (ms * 1e-3) / 1e12
+    n_live = int(np.count_nonzero(np.diff(case.offsets)))
+    bfwd, bdg = algorithmic_bytes(M, H, F, n_live)
+    # dominant kernel: the FC1 grouped GEMM with the SwiGLU epilogue (one launch
+    # per gg_forward_fc1_swiglu call), 4*M*H*F flops per launch.
+    fc1_flops = 4.0 * M * H * F
+    fc1_ms = call_ms["fc1"]
+    achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    roof = {"kernel": "grouped_gemm_kernel<FC1+SwiGLU>", "bound": "mfma", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": load_traffic(args.workload, "fc1"), "avg_launch_ms": fc1_ms,
+            "flops_per_launch": fc1_flops}
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "experts": E, "tokens": case.T, "topk": w.topk,
+                   "routed_rows": M, "hidden": H, "ffn": F, "routing": w.routing,
+                   "parallelism": "single-gpu"},
+        "routed_rows_per_s": M / (ms * 1e-3), "tokens_per_s": case.T / (ms * 1e-3),
+        "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "hbm_GBps_algorithmic": (bfwd + bdg) / (ms * 1e-3) / 1e9,
+        "per_call_ms": call_ms,
+        "roofline": roof,
+        "kernel_source_sha": kernel_source_hash(),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/* gg.h -- C ABI of the MI355X (gfx950) grouped GEMM for frozen MoE experts.
+ *
+ * The library runs, for every local expert e over that expert's contiguous
+ * block of routed token rows, the bias-free gated expert MLP and its input
+ * gradient:
+ *
+ *   forward   H1 = X W1_e^T          [rows, 2F]  gate = H1[:, :F], up = H1[:, F:]
+ *             A  = silu(gate) * up   [rows, F]
+ *             Y  = A W2_e^T          [rows, H]
+ *   dgrad     dA  = dY W2_e                                 [rows, F]
+ *             dH1 = [dA * up * silu'(gate) | dA * silu(gate)] [rows, 2F]
+ *             dX  = dH1 W1_e                                [rows, H]
+ *
+ * with all experts covered by one launch per GEMM, as the Megatron-LM pull
+ * request "perf(moe): add frozen grouped GEMM for adapter training" does in
+ * place of one small GEMM per expert (section "Why this change").  Weights
+ * are frozen, grouped, bias-free BF16 (section "Why existing behavior remains
+ * safe"), so there is no weight gradient.  Per-expert row counts stay on the
+ * device and are never read by the host (TE device-metadata grouped GEMM
+ * pull request, section "Summary").  The gated activation is SwiGLU with the
+ * gate and up halves as two contiguous blocks, not interleaved (paged-stash
+ * pull request, section "What does this PR do").
+ *
+ * Conventions shared by every call
+ *  - Tensors are DEVICE pointers to bf16 bit patterns, row-major, 16-byte
+ *    aligned.  `offsets` is a DEVICE pointer to E+1 int64 values.
+ *  - Rows are sorted by expert: expert e owns rows [offsets[e], offsets[e+1]).
+ *    offsets must be non-decreasing with 0 <= offsets[0] and offsets[E] <= M.
+ *    An expert with offsets[e] == offsets[e+1] has no tokens: nothing is read
+ *    from its weights and nothing is written for it.  The kernels clamp each
+ *    offset into [0, M] and treat a decreasing pair as empty, so bad offsets
+ *    cannot cause an out-of-bounds access (results are then undefined).
+ *  - Outputs are written only at rows [offsets[0], offsets[E]); other rows
+ *    keep their contents.
+ *  - Packed weights: one buffer, expert-major, per expert e
+ *      W1_e [2F][H] at element offset e*3*F*H   (rows 0..F-1 gate, F..2F-1 up)
+ *      W2_e [H][F]  at element offset e*3*F*H + 2*F*H
+ *    (runtime packing of frozen expert weights into one contiguous buffer,
+ *    "Artifacts" and "Why existing behavior remains safe" of the first page).
+ *  - Ownership: the caller owns every buffer.  The library allocates nothing
+ *    on these calls, keeps no pointer after returning, and never synchronises
+ *    the host: every call is asynchronous on `stream`.
+ *  - Errors: every call returns a gg_status and never aborts.  Argument
+ *    checks run before any HIP call.  M == 0 returns GG_OK without a launch.
+ *    A device that is not gfx950 gives GG_ERR_UNSUPPORTED_DEVICE (other
+ *    GPU/library pairs fail explicitly, TE device-metadata pull request,
+ *    "Summary").  Launch failures give GG_ERR_HIP.
+ *  - Limits: 1 <= E <= GG_MAX_EXPERTS; H and F positive multiples of 8;
+ *    M < 2^31.
+ */
+#ifndef GG_H_
+#define GG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GG_MAX_EXPERTS 1024
+
+typedef enum {
+    GG_OK = 0,
+    GG_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, E/H/F/M out of range */
+    GG_ERR_MISALIGNED = 2,         /* a tensor pointer is not 16-byte aligned */
+    GG_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
+    GG_ERR_WORKSPACE_TOO_SMALL = 4,/* packed_bytes or workspace_bytes too small */
+    GG_ERR_ALIASING = 5,           /* an output overlaps an input or another output */
+    GG_ERR_HIP = 6                 /* a HIP runtime call failed */
+} gg_status;
+
+/* Human-readable name of a status code (static string). */
+const char* gg_status_string(int status);
+
+/* Bytes of the packed weight buffer: 6*E*H*F (bf16 W1 and W2 of every expert). */
+size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F);
+
+/* Bytes of the gg_dgrad workspace: dH1 [M][2F] bf16 = 4*M*F. */
+size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F);
+
+/* Pack E experts' frozen weights into `packed` (expert-major layout above).
+ * w1, w2: HOST arrays of E DEVICE pointers; w1[e] -> [2F][H], w2[e] -> [H][F].
+ * A source that already is its destination inside `packed` is skipped, so
+ * re-packing after one expert's weights were replaced copies only what
+ * moved (recovery after a middle expert weight is replaced, "Why existing
+ * behavior remains safe").  A source that partially overlaps `packed` gives
+ * GG_ERR_ALIASING.  Copies are asynchronous device-to-device on `stream`. */
+int gg_pack_weights(int64_t E, int64_t H, int64_t F,
+                    const void* const* w1, const void* const* w2,
+                    void* packed, size_t packed_bytes, hipStream_t stream);
+
+/* Forward FC1 with the fused SwiGLU epilogue.
+ * x [M][H]; packed as above; h1_out [M][2F] (the bf16 FC1 output, saved for
+ * the gradient; may be NULL when no gradient follows); a_out [M][F] =
+ * bf16(silu(gate) * up) computed from the bf16-rounded gate and up. */
+int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M,
+                          const void* packed, int64_t E, int64_t H, int64_t F,
+                          void* h1_out, void* a_out, hipStream_t stream);
+
+/* Forward FC2: y [M][H] = A W2_e^T per expert, a [M][F]. */
+int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M,
+                   const void* packed, int64_t E, int64_t H, int64_t F,
+                   void* y, hipStream_t stream);
+
+/* Input gradient of the whole expert MLP (frozen weights: no weight
+ * gradient; "input gradient" parity of the first page's "Artifacts").
+ * dy [M][H]; h1 [M][2F] as written by gg_forward_fc1_swiglu; workspace of at
+ * least gg_dgrad_workspace_bytes(M, F) bytes receives dH1 [M][2F];
+ * dx [M][H] receives the input gradient.  Two launches on `stream`. */
+int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
+             const void* packed, int64_t E, int64_t H, int64_t F,
+             void* workspace, size_t workspace_bytes, void* dx, hipStream_t stream);
+
+/* Diagnostic: round n fp32 values to bf16 on the device with the same
+ * conversion the epilogues use (lets a test check the device rounding
+ * against round-to-nearest-even).  in: DEVICE float[n]; out: DEVICE
+ * uint16[n]; asynchronous on `stream`. */
+int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GG_H_ */

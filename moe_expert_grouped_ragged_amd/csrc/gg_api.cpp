@@ -1,0 +1,284 @@
+// C-ABI entry points of libgg: argument validation, device checks and
+// kernel launches.  Declarations and the contract are in include/gg.h.
+//
+// Every argument check runs before the first HIP call, so a bad call is
+// rejected on any machine, with or without a GPU.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "gg.h"
+#include "gg_kernels.h"
+
+static_assert(GG_MAX_EXPERTS == GG_KMAX_EXPERTS, "expert limit mismatch");
+
+namespace {
+
+struct DeviceInfo {
+    int checked = 0;      // 0 unknown, 1 gfx950, -1 other
+    int num_cu = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int current_device_info(DeviceInfo* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GG_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GG_ERR_UNSUPPORTED_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (d.checked == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GG_ERR_HIP;
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.num_cu = prop.multiProcessorCount;
+        d.checked = ok ? 1 : -1;
+    }
+    if (d.checked != 1) return GG_ERR_UNSUPPORTED_DEVICE;
+    *out = d;
+    return GG_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) {
+    return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks common to the GEMM calls.
+int check_shape(int64_t M, int64_t E, int64_t H, int64_t F) {
+    if (E < 1 || E > GG_MAX_EXPERTS) return GG_ERR_INVALID_ARGUMENT;
+    if (H <= 0 || F <= 0 || (H % 8) != 0 || (F % 8) != 0) return GG_ERR_INVALID_ARGUMENT;
+    if (H > (int64_t(1) << 24) || F > (int64_t(1) << 24)) return GG_ERR_INVALID_ARGUMENT;
+    if (M < 0 || M >= (int64_t(1) << 31)) return GG_ERR_INVALID_ARGUMENT;
+    return GG_OK;
+}
+
+// Outputs must not overlap any input nor each other.
+int check_aliasing(const std::vector<Range>& ins, const std::vector<Range>& outs) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return GG_ERR_ALIASING;
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlap(outs[i], outs[j])) return GG_ERR_ALIASING;
+    }
+    return GG_OK;
+}
+
+// Optional synchronous check of the device offsets (GG_DEBUG_VALIDATE=1).
+int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStream_t stream) {
+    static const bool on = [] {
+        const char* v = std::getenv("GG_DEBUG_VALIDATE");
+        return v && v[0] == '1';
+    }();
+    if (!on) return GG_OK;
+    std::vector<int64_t> h(static_cast<size_t>(E + 1));
+    if (hipMemcpyAsync(h.data(), offsets, sizeof(int64_t) * (E + 1), hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GG_ERR_HIP;
+    if (h[0] < 0 || h[static_cast<size_t>(E)] > M) return GG_ERR_INVALID_ARGUMENT;
+    for (int64_t e = 0; e < E; ++e)
+        if (h[e + 1] < h[e]) return GG_ERR_INVALID_ARGUMENT;
+    return GG_OK;
+}
+
+gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed, int64_t E,
+                           int64_t H, int64_t F) {
+    gg::GemmParams p{};
+    p.offsets = offsets;
+    p.M = static_cast<int>(M);
+    p.E = static_cast<int>(E);
+    p.w_expert_stride = 3 * F * H;
+    p.w = static_cast<const uint16_t*>(packed);
+    p.up_off = static_cast<int>(F);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gg_status_string(int status) {
+    switch (status) {
+        case GG_OK: return "GG_OK";
+        case GG_ERR_INVALID_ARGUMENT: return "GG_ERR_INVALID_ARGUMENT";
+        case GG_ERR_MISALIGNED: return "GG_ERR_MISALIGNED";
+        case GG_ERR_UNSUPPORTED_DEVICE: return "GG_ERR_UNSUPPORTED_DEVICE (gfx950 required)";
+        case GG_ERR_WORKSPACE_TOO_SMALL: return "GG_ERR_WORKSPACE_TOO_SMALL";
+        case GG_ERR_ALIASING: return "GG_ERR_ALIASING";
+        case GG_ERR_HIP: return "GG_ERR_HIP";
+        default: return "unknown gg_status";
+    }
+}
+
+size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F) {
+    if (E <= 0 || H <= 0 || F <= 0) return 0;
+    return static_cast<size_t>(6) * static_cast<size_t>(E) * static_cast<size_t>(H) *
+           static_cast<size_t>(F);
+}
+
+size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F) {
+    if (M <= 0 || F <= 0) return 0;
+    return static_cast<size_t>(4) * static_cast<size_t>(M) * static_cast<size_t>(F);
+}
+
+int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, const void* const* w2,
+                    void* packed, size_t packed_bytes, hipStream_t stream) {
+    if (E < 1 || E > GG_MAX_EXPERTS || H <= 0 || F <= 0 || (H % 8) || (F % 8))
+        return GG_ERR_INVALID_ARGUMENT;
+    if (!w1 || !w2 || !packed) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(packed)) return GG_ERR_MISALIGNED;
+    const size_t need = gg_packed_bytes(E, H, F);
+    if (packed_bytes < need) return GG_ERR_WORKSPACE_TOO_SMALL;
+    const size_t w1_bytes = static_cast<size_t>(2 * F * H) * 2;
+    const size_t w2_bytes = static_cast<size_t>(H * F) * 2;
+    const size_t per_expert = w1_bytes + w2_bytes;
+    const Range whole = range_of(packed, need);
+    char* base = static_cast<char*>(packed);
+    for (int64_t e = 0; e < E; ++e) {
+        if (!w1[e] || !w2[e]) return GG_ERR_INVALID_ARGUMENT;
+        if ((reinterpret_cast<uintptr_t>(w1[e]) | reinterpret_cast<uintptr_t>(w2[e])) & 1u)
+            return GG_ERR_MISALIGNED;
+        const void* d1 = base + e * per_expert;
+        const void* d2 = base + e * per_expert + w1_bytes;
+        if (w1[e] != d1 && overlap(range_of(w1[e], w1_bytes), whole)) return GG_ERR_ALIASING;
+        if (w2[e] != d2 && overlap(range_of(w2[e], w2_bytes), whole)) return GG_ERR_ALIASING;
+    }
+    DeviceInfo info;
+    const int st = current_device_info(&info);
+    if (st != GG_OK) return st;
+    for (int64_t e = 0; e < E; ++e) {
+        void* d1 = base + e * per_expert;
+        void* d2 = base + e * per_expert + w1_bytes;
+        if (w1[e] != d1 &&
+            hipMemcpyAsync(d1, w1[e], w1_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return GG_ERR_HIP;
+        if (w2[e] != d2 &&
+            hipMemcpyAsync(d2, w2[e], w2_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return GG_ERR_HIP;
+    }
+    return GG_OK;
+}
+
+int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M, const void* packed,
+                          int64_t E, int64_t H, int64_t F, void* h1_out, void* a_out,
+                          hipStream_t stream) {
+    int st = check_shape(M, E, H, F);
+    if (st != GG_OK) return st;
+    if (M == 0) return GG_OK;
+    if (!x || !offsets || !packed || !a_out) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(a_out) || (h1_out && !aligned16(h1_out)) ||
+        (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        return GG_ERR_MISALIGNED;
+    std::vector<Range> ins = {range_of(x, M * H * 2), range_of(packed, gg_packed_bytes(E, H, F)),
+                              range_of(offsets, (E + 1) * 8)};
+    std::vector<Range> outs = {range_of(a_out, M * F * 2)};
+    if (h1_out) outs.push_back(range_of(h1_out, M * 2 * F * 2));
+    if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
+    DeviceInfo info;
+    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
+    gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
+    p.act = static_cast<const uint16_t*>(x);
+    p.K = static_cast<int>(H);
+    p.N = static_cast<int>(F);
+    p.ldw = static_cast<int>(H);
+    p.out0 = static_cast<uint16_t*>(a_out);
+    p.out1 = static_cast<uint16_t*>(h1_out);
+    return gg::launch_fc1_swiglu(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void* packed, int64_t E,
+                   int64_t H, int64_t F, void* y, hipStream_t stream) {
+    int st = check_shape(M, E, H, F);
+    if (st != GG_OK) return st;
+    if (M == 0) return GG_OK;
+    if (!a || !offsets || !packed || !y) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(a) || !aligned16(packed) || !aligned16(y) || (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        return GG_ERR_MISALIGNED;
+    std::vector<Range> ins = {range_of(a, M * F * 2), range_of(packed, gg_packed_bytes(E, H, F)),
+                              range_of(offsets, (E + 1) * 8)};
+    std::vector<Range> outs = {range_of(y, M * H * 2)};
+    if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
+    DeviceInfo info;
+    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
+    gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
+    p.w = static_cast<const uint16_t*>(packed) + 2 * F * H;
+    p.act = static_cast<const uint16_t*>(a);
+    p.K = static_cast<int>(F);
+    p.N = static_cast<int>(H);
+    p.ldw = static_cast<int>(F);
+    p.out0 = static_cast<uint16_t*>(y);
+    return gg::launch_fc2(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
+             int64_t E, int64_t H, int64_t F, void* workspace, size_t workspace_bytes, void* dx,
+             hipStream_t stream) {
+    int st = check_shape(M, E, H, F);
+    if (st != GG_OK) return st;
+    if (M == 0) return GG_OK;
+    if (!dy || !h1 || !offsets || !packed || !workspace || !dx) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dy) || !aligned16(h1) || !aligned16(packed) || !aligned16(workspace) ||
+        !aligned16(dx) || (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        return GG_ERR_MISALIGNED;
+    if (workspace_bytes < gg_dgrad_workspace_bytes(M, F)) return GG_ERR_WORKSPACE_TOO_SMALL;
+    std::vector<Range> ins = {range_of(dy, M * H * 2), range_of(h1, M * 2 * F * 2),
+                              range_of(packed, gg_packed_bytes(E, H, F)), range_of(offsets, (E + 1) * 8)};
+    std::vector<Range> outs = {range_of(workspace, gg_dgrad_workspace_bytes(M, F)),
+                               range_of(dx, M * H * 2)};
+    if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
+    DeviceInfo info;
+    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
+    // dA = dY W2_e, then the SwiGLU derivative with the saved H1 -> dH1 (workspace)
+    gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
+    p.w = static_cast<const uint16_t*>(packed) + 2 * F * H;
+    p.act = static_cast<const uint16_t*>(dy);
+    p.K = static_cast<int>(H);
+    p.N = static_cast<int>(F);
+    p.ldw = static_cast<int>(F);
+    p.aux = static_cast<const uint16_t*>(h1);
+    p.out0 = static_cast<uint16_t*>(workspace);
+    if (gg::launch_dgrad_fc2(p, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
+    // dX = dH1 W1_e
+    gg::GemmParams q = base_params(offsets, M, packed, E, H, F);
+    q.act = static_cast<const uint16_t*>(workspace);
+    q.K = static_cast<int>(2 * F);
+    q.N = static_cast<int>(H);
+    q.ldw = static_cast<int>(H);
+    q.out0 = static_cast<uint16_t*>(dx);
+    return gg::launch_dgrad_fc1(q, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
+    if (n < 0) return GG_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GG_OK;
+    if (!in || !out) return GG_ERR_INVALID_ARGUMENT;
+    if (overlap(range_of(in, n * 4), range_of(out, n * 2))) return GG_ERR_ALIASING;
+    DeviceInfo info;
+    const int st = current_device_info(&info);
+    if (st != GG_OK) return st;
+    return gg::launch_round_bf16(in, out, n, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal interface between the C-ABI entry points and the grouped GEMM
+// kernels (not part of the public ABI; see include/gg.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define GG_KMAX_EXPERTS 1024
+
+namespace gg {
+
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
+
+// One grouped GEMM over all experts: for expert e and its rows r,
+//   out[r, n] = sum_k act[r, k] * Wt_e[n, k]   (Wt_e[n, k] = W_e[n*ldw + k] when the
+//               weights are K-contiguous, W_e[k*ldw + n] for the transposed variant)
+struct GemmParams {
+    const uint16_t* act;       // token operand [M][K] (X, A, dY or dH1), row stride K
+    const uint16_t* w;         // packed weights + in-expert offset of this GEMM's matrix
+    const int64_t* offsets;    // device [E+1]
+    int64_t w_expert_stride;   // elements between consecutive experts (3*F*H)
+    int M, E, K, N;            // N = output columns (F for the SwiGLU variants)
+    int ldw;                   // weight row stride in elements
+    int up_off;                // SwiGLU: row index of the first "up" row of W1 (= F)
+    uint16_t* out0;            // Y / dX, or A (SwiGLU), or dH1 [M][2F] (SwiGLU derivative)
+    uint16_t* out1;            // SwiGLU: H1 [M][2F] or null
+    const uint16_t* aux;       // SwiGLU derivative: saved H1 [M][2F]
+};
+
+hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
+hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
+hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
+hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
+hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+
+}  // namespace gg

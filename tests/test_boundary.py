@@ -1,0 +1,116 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (no GPU
+needed, no compute launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gg.h")
+
+
+def _gg():
+    import moe_expert_grouped_ragged_amd as gg
+    return gg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("gg_pack_weights", "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    gg = _gg()
+    lib = ctypes.CDLL(gg.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gg.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (gg_[a-z0-9_]+)", out.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void) {{ return (int)gg_packed_bytes(1, 8, 8) == 0; }}\n'
+    proc = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-I/opt/rocm/include",
+                           "-D__HIP_PLATFORM_AMD__", "-"], input=src, capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stderr
+
+
+def test_size_helpers():
+    gg = _gg()
+    assert gg.packed_bytes(4, 64, 128) == 6 * 4 * 64 * 128
+    assert gg.dgrad_workspace_bytes(512, 128) == 4 * 512 * 128
+    assert gg.packed_bytes(0, 64, 128) == 0
+    assert gg.lib.gg_status_string(5) == b"GG_ERR_ALIASING"
+
+
+def test_validation_before_any_hip_call():
+    gg = _gg()
+    L = gg.lib
+    INV, MIS, WS, ALI = (gg.GG_ERR_INVALID_ARGUMENT, gg.GG_ERR_MISALIGNED,
+                         gg.GG_ERR_WORKSPACE_TOO_SMALL, gg.GG_ERR_ALIASING)
+    # empty batch succeeds without touching pointers
+    assert L.gg_forward_fc1_swiglu(None, None, 0, None, 4, 64, 128, None, None, None) == 0
+    assert L.gg_forward_fc2(None, None, 0, None, 4, 64, 128, None, None) == 0
+    assert L.gg_dgrad(None, None, None, 0, None, 4, 64, 128, None, 0, None, None) == 0
+    # shapes
+    assert L.gg_forward_fc2(16, 32, 8, 64, 0, 64, 128, 4096, None) == INV          # E < 1
+    assert L.gg_forward_fc2(16, 32, 8, 64, 1025, 64, 128, 4096, None) == INV       # E too large
+    assert L.gg_forward_fc2(16, 32, 8, 64, 4, 60, 128, 4096, None) == INV          # H % 8
+    assert L.gg_forward_fc2(16, 32, 8, 64, 4, 64, 12, 4096, None) == INV           # F % 8
+    assert L.gg_forward_fc2(16, 32, -1, 64, 4, 64, 128, 4096, None) == INV         # M < 0
+    assert L.gg_forward_fc2(16, 32, 1 << 31, 64, 4, 64, 128, 4096, None) == INV    # M too large
+    # null pointers
+    assert L.gg_forward_fc1_swiglu(None, 32, 8, 64, 4, 64, 128, None, 4096, None) == INV
+    assert L.gg_forward_fc1_swiglu(16, 32, 8, 64, 4, 64, 128, None, None, None) == INV
+    assert L.gg_dgrad(16, 4096, 32, 8, 1 << 20, 4, 64, 128, None, 1 << 20, 1 << 24, None) == INV
+    # misalignment
+    base = 1 << 40
+    assert L.gg_forward_fc2(base + 2, base + 2 ** 30, 8, base + 2 ** 31, 4, 64, 128, base + 2 ** 32,
+                            None) == MIS
+    assert L.gg_forward_fc2(base, base + 2 ** 30 + 4, 8, base + 2 ** 31, 4, 64, 128, base + 2 ** 32,
+                            None) == MIS
+    # workspace too small
+    M, H, F = 8, 64, 128
+    need = gg.dgrad_workspace_bytes(M, F)
+    assert L.gg_dgrad(base, base + 2 ** 30, base + 2 ** 31, M, base + 2 ** 32, 4, H, F,
+                      base + 2 ** 33, need - 1, base + 2 ** 34, None) == WS
+    # aliasing: output overlaps an input / another output
+    assert L.gg_forward_fc2(base, base + 2 ** 30, M, base + 2 ** 31, 4, H, F, base + 64, None) == ALI
+    assert L.gg_forward_fc1_swiglu(base, base + 2 ** 30, M, base + 2 ** 31, 4, H, F,
+                                   base + 2 ** 32, base + 2 ** 32 + 16, None) == ALI
+    assert L.gg_dgrad(base, base + 2 ** 30, base + 2 ** 31, M, base + 2 ** 32, 4, H, F,
+                      base + 2 ** 33, need, base + 2 ** 33 + 32, None) == ALI
+    # pack: bad sizes, too small a buffer, a source partially overlapping the buffer
+    P = ctypes.c_void_p
+    arr = (P * 2)(base, base + 2 ** 20)
+    assert L.gg_pack_weights(2, 60, 8, arr, arr, base + 2 ** 32, 1 << 30, None) == INV
+    assert L.gg_pack_weights(2, 64, 8, arr, arr, base + 2 ** 32, 10, None) == WS
+    pk = base + 2 ** 32
+    overl = (P * 2)(pk + 16, pk + 2 ** 16)
+    assert L.gg_pack_weights(2, 64, 8, overl, overl, pk, gg.packed_bytes(2, 64, 8), None) == ALI
+    # diagnostic rounding: negative n
+    assert L.gg_round_bf16(base, base + 2 ** 30, -1, None) == INV
+
+
+def test_python_binding_refuses_unsupported_weights():
+    gg = _gg()
+    import torch
+    w1 = torch.zeros(2, 16, 8, dtype=torch.float32)
+    w2 = torch.zeros(2, 8, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="bfloat16"):
+        gg.gg_pack_weights(w1, w2)
+    w1 = torch.zeros(2, 16, 8, dtype=torch.bfloat16, requires_grad=True)
+    w2 = torch.zeros(2, 8, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="frozen"):
+        gg.gg_pack_weights(w1, w2)

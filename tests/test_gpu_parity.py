@@ -1,0 +1,261 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X only).
+
+Same seeded inputs on both sides; forward (H1, A, Y) and input gradient
+(dH1, dX) compared element by element at the tolerance in parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from gpu_harness import DeviceCase, log
+from parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_ok():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_full_parity(case, check_dgrad_with_oracle_h1=True):
+    """Whole-problem parity (every element)."""
+    _gpu_ok()
+    log(f"[parity] {case.name} E={case.E} H={case.H} F={case.F} M={case.M} counts={list(case.counts)[:16]}")
+    dc = DeviceCase(case)
+    h1, a, y = dc.forward()
+    torch.cuda.synchronize()
+    ref = oracle.forward(case.x, case.offsets, case.w1, case.w2)
+    rows = np.arange(int(case.offsets[0]), int(case.offsets[-1]))
+    out = [check("h1", h1, ref["h1"], rows), check("a", a, ref["a"], rows), check("y", y, ref["y"], rows)]
+    # dgrad from the same saved H1 on both sides (the oracle's), then end to end
+    if check_dgrad_with_oracle_h1:
+        h1_ref = torch.from_numpy(ref["h1"]).to(torch.bfloat16).to(dc.dev)
+        ws, dx = dc.dgrad(h1_ref)
+        torch.cuda.synchronize()
+        dref = oracle.dgrad(case.dy, ref["h1"], case.offsets, case.w1, case.w2)
+        out += [check("dh1", ws, dref["dh1"], rows), check("dx", dx, dref["dx"], rows)]
+    ws2, dx2 = dc.dgrad(h1)
+    torch.cuda.synchronize()
+    dref2 = oracle.dgrad(case.dy, h1.cpu(), case.offsets, case.w1, case.w2)
+    out += [check("dx_e2e", dx2, dref2["dx"], rows)]
+    log(f"[parity] {case.name} ok: " + ", ".join(f"{o['name']} rl2={o.get('rel_l2', 0):.2e} "
+                                                  f"wr={o.get('worst_ratio', 0):.2f}" for o in out))
+    return dc, (h1, a, y, dx2)
+
+
+def test_device_bf16_rounding_exhaustive():
+    """The epilogue's fp32->bf16 conversion over all 2^32 fp32 patterns,
+    against torch's device conversion (round to nearest even), plus a CPU
+    check of a random subset against the oracle's rounding routine."""
+    _gpu_ok()
+    import moe_expert_grouped_ragged_amd as gg
+    chunk = 1 << 28
+    bad = 0
+    for base in range(0, 1 << 32, chunk):
+        bits = torch.arange(base, base + chunk, dtype=torch.int64, device="cuda").to(torch.int32)
+        f = bits.view(torch.float32)
+        got = gg.gg_round_bf16(f).view(torch.int16)
+        want = f.to(torch.bfloat16).view(torch.int16)
+        nan = torch.isnan(f)
+        got_nan = torch.isnan(got.view(torch.bfloat16))
+        mism = (got != want) & ~nan
+        bad += int(mism.sum()) + int((nan & ~got_nan).sum())
+    assert bad == 0
+    rng = np.random.default_rng(0)
+    sample = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    fs = sample.view(np.float32)
+    keep = np.isfinite(fs)
+    fs = fs[keep]
+    got = gg.gg_round_bf16(torch.from_numpy(fs.copy()).cuda()).cpu().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.f32_to_bf16_bits_exact(oracle.round_bf16(fs))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_tiny_workload():
+    run_full_parity(workload.draw_case(workload.by_name("tiny_e4_h64_f128")))
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([1], 64, 64),
+    ([17, 0, 255, 256, 257], 128, 96),
+    ([0, 15, 16, 0, 33, 300, 0], 200, 136),
+    ([513, 0, 0], 72, 264),
+    ([0, 0, 40], 64, 8),
+    ([300, 1, 0, 2, 130], 1024, 256),
+])
+def test_shape_sweep(counts, H, F):
+    run_full_parity(workload.custom_case(counts, H, F, seed=sum(counts) + H + F))
+
+
+def test_padded_segments_zero_rows():
+    case = workload.custom_case([100, 3, 0, 260], 256, 128, seed=7, pad_to=256)
+    dc, (h1, a, y, dx) = run_full_parity(case)
+    for e in range(case.E):
+        pad = slice(int(case.offsets[e] + case.counts[e]), int(case.offsets[e + 1]))
+        for t in (h1, a, y, dx):
+            assert int((t[pad].float() != 0).sum()) == 0
+
+
+def test_zero_experts_everywhere_and_canaries():
+    """Empty experts at first, middle and last position; rows outside
+    [offsets[0], offsets[E]) are canaries that must stay untouched; weights of
+    empty experts are NaN and must not leak."""
+    _gpu_ok()
+    case = workload.custom_case([0, 37, 0, 0, 90, 0], 128, 64, seed=11)
+    M = case.M
+    lead, tail = 5, 7
+    x = torch.cat([torch.ones(lead, case.H, dtype=torch.bfloat16), case.x,
+                   torch.ones(tail, case.H, dtype=torch.bfloat16)])
+    dy = torch.cat([torch.ones(lead, case.H, dtype=torch.bfloat16), case.dy,
+                    torch.ones(tail, case.H, dtype=torch.bfloat16)])
+    w1 = case.w1.clone()
+    w2 = case.w2.clone()
+    for e in (0, 2, 3, 5):
+        w1[e] = float("nan")
+        w2[e] = float("nan")
+    big = workload.Case(case.name, case.E, case.H, case.F, case.T, case.counts, case.offsets + lead,
+                        w1, w2, x, dy)
+    dc = DeviceCase(big)
+    canary = -7.0
+    h1 = torch.full((M + lead + tail, 2 * case.F), canary, dtype=torch.bfloat16, device="cuda")
+    a = torch.full((M + lead + tail, case.F), canary, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((M + lead + tail, case.H), canary, dtype=torch.bfloat16, device="cuda")
+    dc.forward(h1_out=h1, a_out=a, y=y)
+    ws = torch.full((M + lead + tail, 2 * case.F), canary, dtype=torch.bfloat16, device="cuda")
+    dx = torch.full((M + lead + tail, case.H), canary, dtype=torch.bfloat16, device="cuda")
+    dc.dgrad(h1, workspace=ws, dx=dx)
+    torch.cuda.synchronize()
+    for t in (h1, a, y, ws, dx):
+        assert bool((t[:lead] == canary).all()) and bool((t[lead + M:] == canary).all())
+        assert bool(torch.isfinite(t[lead:lead + M].float()).all())
+    ref = oracle.forward(case.x, case.offsets, case.w1, case.w2)
+    check("y", y[lead:lead + M], ref["y"])
+    dref = oracle.dgrad(case.dy, h1[lead:lead + M].cpu(), case.offsets, case.w1, case.w2)
+    check("dx", dx[lead:lead + M], dref["dx"])
+
+
+def test_all_experts_empty_and_empty_batch():
+    _gpu_ok()
+    import moe_expert_grouped_ragged_amd as gg
+    E, H, F, M = 4, 64, 64, 32
+    off = torch.zeros(E + 1, dtype=torch.int64, device="cuda")
+    packed = torch.zeros(3 * E * F * H, dtype=torch.bfloat16, device="cuda")
+    x = torch.randn(M, H, device="cuda").to(torch.bfloat16)
+    a = torch.full((M, F), 3.0, dtype=torch.bfloat16, device="cuda")
+    h1 = torch.full((M, 2 * F), 3.0, dtype=torch.bfloat16, device="cuda")
+    gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
+    y = torch.full((M, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
+    torch.cuda.synchronize()
+    assert bool((a == 3.0).all()) and bool((h1 == 3.0).all()) and bool((y == 3.0).all())
+    # M = 0: success, nothing launched
+    x0 = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    h, a0 = gg.gg_forward_fc1_swiglu(x0, off, packed, E, H, F)
+    assert a0.shape == (0, F)
+
+
+def test_determinism_and_grouped_equals_per_expert():
+    """Two runs are bitwise equal; a grouped call equals per-expert calls
+    (E = 1 views of the packed buffer) bitwise."""
+    _gpu_ok()
+    import moe_expert_grouped_ragged_amd as gg
+    case = workload.custom_case([70, 0, 300, 5], 256, 192, seed=13)
+    dc = DeviceCase(case)
+    h1, a, y = dc.forward()
+    ws, dx = dc.dgrad(h1)
+    h1b, ab, yb = dc.forward()
+    wsb, dxb = dc.dgrad(h1b)
+    torch.cuda.synchronize()
+    for p, q in ((h1, h1b), (a, ab), (y, yb), (ws, wsb), (dx, dxb)):
+        assert torch.equal(p.view(torch.int16), q.view(torch.int16))
+    per = 3 * case.F * case.H
+    for e in range(case.E):
+        s, t = int(case.offsets[e]), int(case.offsets[e + 1])
+        if s == t:
+            continue
+        pk = dc.packed[e * per:(e + 1) * per]
+        off1 = torch.tensor([0, t - s], dtype=torch.int64, device="cuda")
+        h1e, ae = gg.gg_forward_fc1_swiglu(dc.x[s:t].contiguous(), off1, pk, 1, case.H, case.F)
+        ye = gg.gg_forward_fc2(ae, off1, pk, 1, case.H, case.F)
+        dxe = gg.gg_dgrad(dc.dy[s:t].contiguous(), h1e, off1, pk, 1, case.H, case.F)
+        torch.cuda.synchronize()
+        assert torch.equal(ye.view(torch.int16), y[s:t].view(torch.int16))
+        assert torch.equal(dxe.view(torch.int16), dx[s:t].view(torch.int16))
+
+
+def test_repack_after_middle_expert_replaced():
+    _gpu_ok()
+    import moe_expert_grouped_ragged_amd as gg
+    case = workload.custom_case([20, 30, 40], 64, 64, seed=17)
+    dc = DeviceCase(case)
+    w1v, w2v = gg.expert_views(dc.packed, case.E, case.H, case.F)
+    # views into the packed buffer re-pack as a no-op
+    gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
+    y0 = dc.forward()[2].clone()
+    new_w1 = workload.custom_case([1], 64, 64, seed=99).w1[0].cuda()
+    w1v = list(w1v)
+    w1v[1] = new_w1                       # the middle expert is replaced by a new tensor
+    gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
+    y1 = dc.forward()[2]
+    torch.cuda.synchronize()
+    s1, t1 = int(case.offsets[1]), int(case.offsets[2])
+    assert torch.equal(y1[:s1], y0[:s1]) and torch.equal(y1[t1:], y0[t1:])
+    w1 = case.w1.clone()
+    w1[1] = new_w1.cpu()
+    ref = oracle.forward(case.x, case.offsets, w1, case.w2)
+    check("y_repacked", y1, ref["y"])
+
+
+def _sampled_rows(case, per_expert=3, max_experts=24, seed=0):
+    rng = np.random.default_rng(seed)
+    off = case.offsets
+    live = [e for e in range(case.E) if off[e + 1] > off[e]]
+    sizes = np.array([off[e + 1] - off[e] for e in live])
+    pick = set(live[:2] + live[-2:] + [live[int(np.argmax(sizes))], live[int(np.argmin(sizes))]])
+    rest = [e for e in live if e not in pick]
+    rng.shuffle(rest)
+    pick = sorted(pick | set(rest[:max(0, max_experts - len(pick))]))
+    rows = []
+    for e in pick:
+        s, t = int(off[e]), int(off[e + 1])
+        cand = {s, t - 1} | set(int(v) for v in rng.integers(s, t, per_expert))
+        rows += sorted(cand)
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["uniform_e32_h2048_f768", "zipf_e128_h2048_f768",
+                                  "smallbatch_e128_h2688_f1856", "padded_e128_h4096_f2048"])
+def test_workload_sampled_rows(name):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    computes a sample of rows (first/last row of chosen experts plus random
+    rows), every row depending only on its own inputs and expert."""
+    _gpu_ok()
+    w = workload.by_name(name)
+    log(f"[sampled] drawing {name}")
+    case = workload.draw_case(w)
+    log(f"[sampled] {name} M={case.M}; running GPU")
+    dc = DeviceCase(case)
+    h1, a, y = dc.forward()
+    ws, dx = dc.dgrad(h1)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(case)
+    log(f"[sampled] {name}: oracle on {rows.size} rows")
+    expert, compact = oracle.sample_rows(case.offsets, rows)
+    xs = case.x[torch.from_numpy(rows)]
+    ref = oracle.forward(xs, compact, case.w1, case.w2)
+    check("h1", h1[torch.from_numpy(rows).cuda()], ref["h1"])
+    check("y", y[torch.from_numpy(rows).cuda()], ref["y"])
+    h1s = h1[torch.from_numpy(rows).cuda()].cpu()
+    dys = case.dy[torch.from_numpy(rows)]
+    dref = oracle.dgrad(dys, h1s, compact, case.w1, case.w2)
+    check("dh1", ws[torch.from_numpy(rows).cuda()], dref["dh1"])
+    check("dx", dx[torch.from_numpy(rows).cuda()], dref["dx"])
+    # padding rows (if any) are exact zeros everywhere
+    for e in range(case.E):
+        pad = slice(int(case.offsets[e] + case.counts[e]), int(case.offsets[e + 1]))
+        if pad.stop > pad.start:
+            assert int((y[pad].float() != 0).sum()) == 0 and int((dx[pad].float() != 0).sum()) == 0
+    log(f"[sampled] {name} ok")
