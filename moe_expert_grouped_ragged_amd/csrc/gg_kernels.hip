@@ -7,23 +7,31 @@
 // request, section "Summary"), and then walks the global tile list.  Experts
 // with no rows own no tiles, so their weights are never read.
 //
-// The tile core is a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
-// accumulators) with both operands staged through LDS in a [row][k] layout
-// whose 16-byte chunks are XOR-swizzled by row, double-buffered so the next
-// K panel is loaded from HBM while the current one feeds the matrix cores.
+// Tile core: bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  Both
+// operand panels stream from HBM straight into LDS with LDS-DMA loads
+// (global_load_lds_dwordx4, 16 bytes per lane) through an NS-stage ring, so
+// several K panels are in flight while the matrix cores work on an earlier
+// one; one barrier per K step.
+//  - K-contiguous panels (tokens; forward weights) sit in LDS as [row][32 k]
+//    with the four 16-byte chunks of a row XOR-swizzled by (row >> 1) & 3;
+//    fragments are read with ds_read_b128.
+//  - The transposed-weight variant (dgrad) reads W as [K][N] (N contiguous):
+//    the panel lands in LDS as [32 k][BN n] with 16-byte chunks swizzled by
+//    2 * (k & 3) and the MFMA operand is assembled with two
+//    ds_read_b64_tr_b16 per fragment, which transpose 4x16 blocks of 16-bit
+//    elements across each group of 16 lanes.
 // The weight side is the MFMA "A" operand and the token side the "B"
 // operand, so each lane ends up holding one token row and four groups of
 // four consecutive output columns: stores are 8-byte vectors.
 //
 // Variants (template parameter EPI and W_KN):
-//   FC1 + SwiGLU  W_KN=false  weights W1_e [2F][H] (K-contiguous); a tile
-//                 loads matching gate rows n.. and up rows F+n.. so SwiGLU
-//                 is applied in registers; writes H1 (optional) and A.
+//   FC1 + SwiGLU  W_KN=false  weights W1_e [2F][H]; a tile loads matching gate
+//                 rows n.. and up rows F+n.. so SwiGLU is applied in
+//                 registers; writes H1 (optional) and A.
 //   FC2           W_KN=false  weights W2_e [H][F]; writes Y.
-//   dgrad FC2     W_KN=true   dA = dY W2_e: the contraction runs over W2's
-//                 rows, so the weight panel arrives [K][N] and is transposed
-//                 in registers on its way into LDS; the epilogue applies the
-//                 SwiGLU derivative with the saved H1 and writes dH1.
+//   dgrad FC2     W_KN=true   dA = dY W2_e (contraction over W2's rows); the
+//                 epilogue applies the SwiGLU derivative with the saved H1
+//                 and writes dH1.
 //   dgrad FC1     W_KN=true   dX = dH1 W1_e; writes dX.
 // Rounding points mirror the unfused computation: H1, A, Y, dA, dH1 and dX
 // are each rounded once to bf16 (round to nearest even); SwiGLU and its
@@ -37,10 +45,12 @@
 namespace gg {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BK = 64;          // K elements per LDS panel (128 bytes per row)
-constexpr int CHUNKS = BK / 8;  // 16-byte chunks per panel row
+#define GG_AS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int BK = 32;  // K elements per pipeline stage
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -52,9 +62,69 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
 }
 
-// Element offset of 16-byte chunk `ch` of panel row `row` (swizzled).
-__device__ __forceinline__ int lds_off(int row, int ch) {
-    return row * BK + ((ch ^ (row & 7)) << 3);
+// Chunk swizzles (chosen from LDS bank-conflict counter measurements on
+// gfx950).  K-contiguous panels are [row][32 k] (64-byte rows, four 16-byte
+// chunks); chunk c of row r is stored at c ^ kswz(r), which keeps the
+// 16-byte fragment reads (32 rows x 2 chunks per wave) conflict-free.
+// N-contiguous panels are [32 k][BN n]; chunk c of row k is stored at
+// c ^ nswz(k), which keeps the 8-byte transpose reads conflict-free (it
+// permutes 4-chunk blocks, so column offsets of 16 chunks stay additive).
+__device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int nswz(int k) { return (k & 3) << 2; }
+
+// [row][32] K-contiguous panel: element offset of logical 16-byte chunk c (0..3) of `row`.
+__device__ __forceinline__ int kc_off(int row, int c) {
+    return row * BK + ((c ^ kswz(row)) << 3);
+}
+// [32][BN] N-contiguous panel: element offset of column n (multiple of 4) in row k.
+template <int BN>
+__device__ __forceinline__ int nc_off(int k, int n) {
+    return k * BN + (((n >> 3) ^ nswz(k)) << 3) + (n & 7);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One wave-wide LDS-DMA load: every lane copies 16 bytes from base + voff
+// (base wave-uniform, voff a per-lane 32-bit byte offset) to LDS byte address
+// lds + 16 * lane (lds wave-uniform).  Issued from
+// inline assembly so that the compiler does not add a conservative wait for
+// all outstanding loads before every LDS read; the pipeline waits for the
+// stage it needs explicitly (wait_vmcnt + barrier).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read one accumulator register in the epilogue.  The accumulators live in
+// AGPRs; reading them one at a time where they are consumed keeps the
+// compiler from copying all of them to VGPRs at once at the end of the K loop.
+__device__ __forceinline__ float acc_rd(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(GG_AS3(const_cast<T*>(p)))));
 }
 
 template <int NT>
@@ -104,39 +174,45 @@ __device__ __forceinline__ int find_expert(const int* s_pre, int E, int t) {
     return lo;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool W_KN, int EPI>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
-void grouped_gemm_kernel(const GemmParams p) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
-    constexpr int WTM = BM / WAVES_M;           // token rows per wave
-    constexpr int WTN = BN / WAVES_N;           // weight rows per wave
-    constexpr int TM = WTM / 32;
-    constexpr int TN = WTN / 32;
-    constexpr int A_CHUNKS = BM * CHUNKS / NT;  // 16-byte token chunks per thread per panel
-    constexpr int B_CHUNKS = BN * CHUNKS / NT;  // (K-contiguous weights)
-    constexpr int B_BLOCKS = (BK / 4) * (BN / 8) / NT;  // 4x8 blocks per thread ([K][N] weights)
-    static_assert(BM * CHUNKS % NT == 0 && BN * CHUNKS % NT == 0, "tile/threads");
-    static_assert(!W_KN || ((BK / 4) * (BN / 8)) % NT == 0, "tile/threads");
-    static_assert(EPI != EPI_SWIGLU || (TN % 2 == 0), "SwiGLU needs gate/up pairs per wave");
+// Tile geometry: a workgroup computes a 256 (token rows) x 256 (weight rows)
+// output tile with 8 waves, two per SIMD.  Wave w belongs to group g = w / 4
+// (token rows g*128 .. g*128+127) and owns 64 weight rows (w % 4); waves w and
+// w + 4 share a SIMD.  The two groups alternate ("ping-pong"): while one
+// group issues its MFMAs for a K stage, the other reads its fragments for
+// that stage from LDS and issues the HBM->LDS copies, and a barrier swaps the
+// roles, so the matrix pipe of every SIMD always has a wave feeding it.
+template <int V> struct GrpTag { static constexpr int value = V; };
+constexpr int TBM = 256, TBN = 256, NWAVES = 8, NTHREADS = NWAVES * 64, NSTAGE = 4;
+constexpr int WROWS = 128, WCOLS = 64, FM = WROWS / 32, FN = WCOLS / 32;
+constexpr int A_STAGE = TBM * BK, B_STAGE = TBN * BK;          // elements per stage
+constexpr int A_PW = A_STAGE * 2 / 1024 / NWAVES;               // 1 KiB DMA instructions per wave
+constexpr int B_PW = B_STAGE * 2 / 1024 / NWAVES;
+constexpr int LPS = A_PW + B_PW;                                // per wave per stage
+static_assert(A_PW * NWAVES * 1024 == A_STAGE * 2 && B_PW * NWAVES * 1024 == B_STAGE * 2, "DMA split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * BK];
+template <bool W_KN, int EPI>
+__global__ __launch_bounds__(NTHREADS)
+void grouped_gemm_kernel(const GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s_a[NSTAGE][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_b[NSTAGE][B_STAGE];
     __shared__ int s_off[GG_KMAX_EXPERTS + 1];
     __shared__ int s_pre[GG_KMAX_EXPERTS + 1];
 
     const int E = p.E, M = p.M, K = p.K, N = p.N;
-    // output columns covered by one tile
-    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int tiles_n = (N + TILE_COLS - 1) / TILE_COLS;
-    build_schedule<NT>(p.offsets, E, M, BM, tiles_n, s_off, s_pre);
+    build_schedule<NTHREADS>(p.offsets, E, M, TBM, tiles_n, s_off, s_pre);
     const int total = s_pre[E];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WAVES_N;
-    const int wn = wave % WAVES_N;
+    const int wave = uni(tid >> 6);
+    const int grp = wave >> 2;          // 0: token rows 0..127, 1: 128..255
+    const int wq = wave & 3;            // weight-row block
     const int kiters = (K + BK - 1) / BK;
+    const bool k_tail = (K % BK) != 0;
+    const uint32_t a_lds0 = lds_addr(&s_a[0][0]) + wave * A_PW * 1024;
+    const uint32_t b_lds0 = lds_addr(&s_b[0][0]) + wave * B_PW * 1024;
 
     // Workgroups are dealt round-robin over the 8 XCDs; give the workgroups of
     // one XCD consecutive tiles so that tiles sharing panels share an L2.
@@ -144,248 +220,383 @@ void grouped_gemm_kernel(const GemmParams p) {
     const int b = blockIdx.x;
     const int slot = (G % 8 == 0) ? (b & 7) * (G >> 3) + (b >> 3) : b;
 
-    for (int t = slot; t < total; t += G) {
-        const int e = find_expert(s_pre, E, t);
-        const int local = t - s_pre[e];
-        const int row_beg = s_off[e];
-        const int row_end = s_off[e + 1];
-        const int tiles_m = (row_end - row_beg + BM - 1) / BM;
-        const int tm = local % tiles_m;
-        const int tn = local / tiles_m;
-        const int row0 = row_beg + tm * BM;
-        const int col0 = tn * TILE_COLS;
-        const uint16_t* __restrict__ w = p.w + static_cast<int64_t>(e) * p.w_expert_stride;
-        const uint16_t* __restrict__ act = p.act;
+    // ---- per-tile state (wave-uniform values live in SGPRs)
+    int row0 = 0, row_end = 0, col0 = 0;
+    const uint16_t* a_base = p.act;   // first row of the tile
+    const uint16_t* w_base = p.w;     // this expert's weight matrix
+    uint32_t a_voff[A_PW];            // byte offset of the chunk this lane moves (k0 = 0)
+    uint32_t b_voff[B_PW];
+    int a_kc[A_PW];                   // k offset of the chunk (K-contiguous)
+    int b_kc[B_PW];                   // k offset (K-contiguous) / panel row (N-contiguous)
 
-        // ---- per-thread global source pointers for the token panel
-        const uint16_t* a_src[A_CHUNKS];
-        int a_kc[A_CHUNKS];
-        int a_dst[A_CHUNKS];
+    auto setup_tile = [&](int t) {
+        const int e = uni(find_expert(s_pre, E, t));
+        const int local = t - uni(s_pre[e]);
+        const int rb = uni(s_off[e]);
+        row_end = uni(s_off[e + 1]);
+        const int tiles_m = (row_end - rb + TBM - 1) / TBM;
+        row0 = rb + (local % tiles_m) * TBM;
+        col0 = (local / tiles_m) * TILE_COLS;
+        a_base = p.act + static_cast<int64_t>(row0) * K;
+        w_base = p.w + static_cast<int64_t>(e) * p.w_expert_stride;
+        const int rows = row_end - row0;
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int idx = tid + i * NT;
-            const int r = idx / CHUNKS, ch = idx % CHUNKS;
-            const int grow = min(row0 + r, row_end - 1);
-            a_src[i] = act + static_cast<int64_t>(grow) * K + ch * 8;
-            a_kc[i] = ch * 8;
-            a_dst[i] = lds_off(r, ch);
+        for (int i = 0; i < A_PW; ++i) {
+            const int pos = (wave * A_PW + i) * 64 + lane;   // 16-byte chunk slot in the stage
+            const int r = pos >> 2;
+            const int c = (pos & 3) ^ kswz(r);                 // logical chunk stored there
+            a_voff[i] = static_cast<uint32_t>((min(r, rows - 1) * K + c * 8) * 2);
+            a_kc[i] = c * 8;
         }
-        // ---- weight panel sources
-        const uint16_t* b_src[W_KN ? B_BLOCKS : B_CHUNKS];
-        int b_kc[W_KN ? B_BLOCKS : B_CHUNKS];
-        int b_dst[W_KN ? B_BLOCKS : B_CHUNKS];
-        if constexpr (!W_KN) {
 #pragma unroll
-            for (int i = 0; i < B_CHUNKS; ++i) {
-                const int idx = tid + i * NT;
-                const int r = idx / CHUNKS, ch = idx % CHUNKS;
+        for (int i = 0; i < B_PW; ++i) {
+            const int pos = (wave * B_PW + i) * 64 + lane;
+            if constexpr (!W_KN) {
+                const int r = pos >> 2;
+                const int c = (pos & 3) ^ kswz(r);
                 int wrow;
                 if constexpr (EPI == EPI_SWIGLU) {
-                    const int half = r / (BN / 2);
-                    const int c = min(col0 + r % (BN / 2), N - 1);
-                    wrow = c + half * p.up_off;
+                    const int half = r / (TBN / 2);
+                    wrow = min(col0 + r % (TBN / 2), N - 1) + half * p.up_off;
                 } else {
                     wrow = min(col0 + r, N - 1);
                 }
-                b_src[i] = w + static_cast<int64_t>(wrow) * p.ldw + ch * 8;
-                b_kc[i] = ch * 8;
-                b_dst[i] = lds_off(r, ch);
+                b_voff[i] = static_cast<uint32_t>((wrow * p.ldw + c * 8) * 2);
+                b_kc[i] = c * 8;
+            } else {
+                constexpr int CPR = TBN / 8;                   // chunks per panel row
+                const int k = pos / CPR;
+                const int c = (pos % CPR) ^ nswz(k);
+                b_voff[i] = static_cast<uint32_t>((k * p.ldw + min(col0 + c * 8, N - 8)) * 2);
+                b_kc[i] = k;
+            }
+        }
+    };
+
+    // Copy K stage kt of both panels into its LDS slot (this wave's share).
+    auto issue = [&](int kt) {
+        const int stage = kt % NSTAGE;
+        const int k0 = kt * BK;
+        const bool tail = k_tail && kt == kiters - 1;
+#pragma unroll
+        for (int i = 0; i < A_PW; ++i) {
+            const uint32_t lds = a_lds0 + stage * (A_STAGE * 2) + i * 1024;
+            if (!tail) {
+                dma16(a_base + k0, a_voff[i], lds);
+            } else {
+                // chunks at k >= K re-read k = 0 of the same row (in bounds); zeroed later
+                const uint32_t v = (k0 + a_kc[i] < K) ? a_voff[i] + k0 * 2 : a_voff[i] - a_kc[i] * 2;
+                dma16(a_base, v, lds);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_PW; ++i) {
+            const uint32_t lds = b_lds0 + stage * (B_STAGE * 2) + i * 1024;
+            if constexpr (!W_KN) {
+                if (!tail) {
+                    dma16(w_base + k0, b_voff[i], lds);
+                } else {
+                    const uint32_t v = (k0 + b_kc[i] < K) ? b_voff[i] + k0 * 2 : b_voff[i] - b_kc[i] * 2;
+                    dma16(w_base, v, lds);
+                }
+            } else {
+                if (!tail) {
+                    dma16(w_base + static_cast<int64_t>(k0) * p.ldw, b_voff[i], lds);
+                } else {
+                    // rows >= K re-read row K-1 (in bounds); zeroed later
+                    const int row = min(k0 + b_kc[i], K - 1);
+                    const uint32_t v = b_voff[i] + static_cast<uint32_t>((row - b_kc[i]) * p.ldw * 2);
+                    dma16(w_base, v, lds);
+                }
+            }
+        }
+    };
+
+    // Wait until this wave's copies of a stage have landed, given how many later
+    // stages it has in flight.
+    auto wait_stage = [&](int newer) {
+        if (newer <= 0) wait_vmcnt<0>();
+        else if (newer == 1) wait_vmcnt<LPS>();
+        else if (newer == 2) wait_vmcnt<2 * LPS>();
+        else wait_vmcnt<3 * LPS>();
+    };
+
+    // Zero the K positions >= K of a stage (only when K % BK != 0, last stage).
+    auto zero_tail = [&](int kt) {
+        const int stage = kt % NSTAGE;
+        const int k0 = kt * BK;
+        for (int idx = tid; idx < TBM * 4; idx += NTHREADS) {
+            const int r = idx >> 2, c = idx & 3;
+            if (k0 + c * 8 >= K)
+                *reinterpret_cast<uint4*>(&s_a[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
+        }
+        if constexpr (!W_KN) {
+            for (int idx = tid; idx < TBN * 4; idx += NTHREADS) {
+                const int r = idx >> 2, c = idx & 3;
+                if (k0 + c * 8 >= K)
+                    *reinterpret_cast<uint4*>(&s_b[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
             }
         } else {
-#pragma unroll
-            for (int i = 0; i < B_BLOCKS; ++i) {
-                const int idx = tid + i * NT;
-                const int kb = idx / (BN / 8), nb = idx % (BN / 8);
-                const int c = min(col0 + nb * 8, N - 8);
-                b_src[i] = w + static_cast<int64_t>(kb * 4) * p.ldw + c;
-                b_kc[i] = kb * 4;
-                b_dst[i] = nb * 8 * BK + kb * 4;   // row nb*8 (+cc), k = kb*4: swizzled below
+            for (int idx = tid; idx < BK * TBN / 8; idx += NTHREADS) {
+                const int k = idx / (TBN / 8), c = idx % (TBN / 8);
+                if (k0 + k >= K)
+                    *reinterpret_cast<uint4*>(&s_b[stage][k * TBN + c * 8]) = make_uint4(0, 0, 0, 0);
             }
         }
+    };
 
-        uint4 ra[A_CHUNKS];
-        uint4 rb[W_KN ? B_BLOCKS * 4 : B_CHUNKS];
+    // column (relative to the tile) of local 16-byte chunk c (0..7) of a wave's
+    // 64 output columns: fragment j = c / 4 sits in tile half j
+    auto wcol = [&](int c) -> int { return (c >> 2) * (TBN / 2) + wq * 32 + (c & 3) * 8; };
 
-        auto load_panel = [&](int kt) {
-            const int k0 = kt * BK;
+    // first weight-panel row (K-contiguous) or column (N-contiguous) of fragment j
+    auto wfrag = [&](int j) -> int {
+        if constexpr (EPI == EPI_SWIGLU) {
+            return j == 0 ? wq * 32 : TBN / 2 + wq * 32;     // gate rows, matching up rows
+        } else {
+            return j * (TBN / 2) + wq * 32;   // 32 columns in each half of the tile
+        }
+    };
+
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto load_frags = [&](int kt) {
+        const uint16_t* sa = s_a[kt % NSTAGE];
+        const uint16_t* sb = s_b[kt % NSTAGE];
 #pragma unroll
-            for (int i = 0; i < A_CHUNKS; ++i) {
-                ra[i] = (k0 + a_kc[i] < K) ? *reinterpret_cast<const uint4*>(a_src[i] + k0)
-                                           : make_uint4(0, 0, 0, 0);
+        for (int ss = 0; ss < 2; ++ss) {
+            const int ch = ss * 2 + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = grp * WROWS + i * 32 + (lane & 31);
+                fa[ss][i] = *reinterpret_cast<const bf16x8*>(sa + kc_off(r, ch));
             }
-            if constexpr (!W_KN) {
 #pragma unroll
-                for (int i = 0; i < B_CHUNKS; ++i) {
-                    rb[i] = (k0 + b_kc[i] < K) ? *reinterpret_cast<const uint4*>(b_src[i] + k0)
-                                               : make_uint4(0, 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < B_BLOCKS; ++i) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int k = k0 + b_kc[i] + r;
-                        rb[i * 4 + r] = (k < K) ? *reinterpret_cast<const uint4*>(
-                                                      b_src[i] + static_cast<int64_t>(k0 + r) * p.ldw)
-                                                : make_uint4(0, 0, 0, 0);
-                    }
-                }
-            }
-        };
-
-        auto store_panel = [&](int buf) {
-            uint16_t* sa = s_a[buf];
-            uint16_t* sb = s_b[buf];
-#pragma unroll
-            for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<uint4*>(sa + a_dst[i]) = ra[i];
-            if constexpr (!W_KN) {
-#pragma unroll
-                for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<uint4*>(sb + b_dst[i]) = rb[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < B_BLOCKS; ++i) {
-                    // rb[i*4 + r] holds row k = kb*4 + r, columns nb*8 .. nb*8+7.
-                    const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&rb[i * 4 + 0]);
-                    const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&rb[i * 4 + 1]);
-                    const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&rb[i * 4 + 2]);
-                    const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&rb[i * 4 + 3]);
-                    const int nrow0 = b_dst[i] / BK;     // nb*8
-                    const int kq = b_kc[i];              // kb*4
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // column 2j (low halves) and 2j+1 (high halves)
-                        uint2 lo, hi;
-                        lo.x = (q0[j] & 0xffffu) | (q1[j] << 16);
-                        lo.y = (q2[j] & 0xffffu) | (q3[j] << 16);
-                        hi.x = (q0[j] >> 16) | (q1[j] & 0xffff0000u);
-                        hi.y = (q2[j] >> 16) | (q3[j] & 0xffff0000u);
-                        const int n_lo = nrow0 + 2 * j, n_hi = n_lo + 1;
-                        const int ch = kq >> 3, sub = kq & 7;
-                        *reinterpret_cast<uint2*>(sb + lds_off(n_lo, ch) + sub) = lo;
-                        *reinterpret_cast<uint2*>(sb + lds_off(n_hi, ch) + sub) = hi;
-                    }
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (!W_KN) {
+                    const int r = wfrag(j) + (lane & 31);
+                    fb[ss][j] = *reinterpret_cast<const bf16x8*>(sb + kc_off(r, ch));
+                } else {
+                    // lane 16g + 4s + q supplies (k = kb + s, n = nb + 4q) and receives
+                    // column nb + (lane & 15), rows kb .. kb+3 (ds_read_b64_tr_b16).
+                    const int g = lane >> 4;
+                    const int kb = ss * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
+                    const int n = wfrag(j) + 16 * (g & 1) + 4 * (lane & 3);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
+                            GG_AS3(sb + nc_off<TBN>(kb, n))));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
+                            GG_AS3(sb + nc_off<TBN>(kb + 4, n))));
+                    const __attribute__((ext_vector_type(8))) short v8 =
+                        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    fb[ss][j] = __builtin_bit_cast(bf16x8, v8);
                 }
             }
-        };
+        }
+    };
 
-        f32x16 acc[TM][TN];
+    f32x16 acc[FM][FN];
+    auto mma = [&]() {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ss][j], fa[ss][i], acc[i][j], 0, 0, 0);
+    };
 
-        // weight-panel row of this wave's j-th 32-row fragment
-        auto wfrag_row = [&](int j) -> int {
-            if constexpr (EPI == EPI_SWIGLU) {
-                constexpr int HALF = TN / 2;
-                return (j < HALF) ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - HALF) * 32;
-            } else {
-                return wn * WTN + j * 32;
-            }
-        };
-
-        load_panel(0);
-        store_panel(0);
-        __syncthreads();
-        for (int kt = 0; kt < kiters; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < kiters) load_panel(kt + 1);
-            const uint16_t* sa = s_a[cur];
-            const uint16_t* sb = s_b[cur];
+    for (int t = slot; t < total; t += G) {
+        setup_tile(t);
 #pragma unroll
-            for (int s = 0; s < BK / 16; ++s) {
-                const int ch = s * 2 + (lane >> 5);
-                bf16x8 fa[TM], fb[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int r = wm * WTM + i * 32 + (lane & 31);
-                    fa[i] = *reinterpret_cast<const bf16x8*>(sa + lds_off(r, ch));
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int r = wfrag_row(j) + (lane & 31);
-                    fb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_off(r, ch));
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < kiters) store_panel(cur ^ 1);
+        for (int s = 0; s < NSTAGE; ++s)
+            if (s < kiters) issue(s);
+        wait_stage(min(NSTAGE - 1, kiters - 1));
+        block_barrier();
+        if (k_tail && kiters == 1) {
+            zero_tail(0);
             __syncthreads();
         }
+        // The two groups run the same barrier sequence (two per K stage) on
+        // separate code paths so that each keeps its fragments in fixed registers.
+        auto mid_stage = [&](int kt) {
+            if (kt + 1 < kiters) wait_stage(min(NSTAGE - 2, kiters - 2 - kt));   // stage kt+1 landed
+            block_barrier();
+            // stage kt is consumed by both groups: refill its slot
+            if (kt + NSTAGE < kiters) issue(kt + NSTAGE);
+            if (k_tail && kt + 1 == kiters - 1) {
+                zero_tail(kt + 1);
+                __syncthreads();
+            }
+        };
+        auto run_group = [&](auto gtag) {
+        constexpr int GRP = decltype(gtag)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        if constexpr (GRP == 0) {
+            load_frags(0);
+            for (int kt = 0; kt < kiters; ++kt) {
+                __builtin_amdgcn_sched_barrier(0);
+                mma();                                   // phase 0: compute stage kt
+                __builtin_amdgcn_sched_barrier(0);
+                mid_stage(kt);
+                if (kt + 1 < kiters) load_frags(kt + 1); // phase 1: read stage kt+1
+                __builtin_amdgcn_sched_barrier(0);
+                block_barrier();
+            }
+        } else {
+            for (int kt = 0; kt < kiters; ++kt) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_frags(kt);                          // phase 0: read stage kt
+                __builtin_amdgcn_sched_barrier(0);
+                mid_stage(kt);
+                mma();                                   // phase 1: compute stage kt
+                __builtin_amdgcn_sched_barrier(0);
+                block_barrier();
+            }
+        }
 
-        // ---- epilogue: lane holds token row (lane & 31) of each token fragment and,
-        // for register v, weight-panel row (v/4)*8 + (lane/32)*4 + v%4.
-        const int cbase = (lane >> 5) * 4;
+        // Values derived below are computed here, not hoisted above the K loop
+        // (that would keep them live in registers across it).
+        int opaque = 0;
+        asm volatile("" : "+s"(opaque));
+        const int c_row0 = row0 + opaque, c_row_end = row_end, c_col0 = col0 + opaque;
+
+        // ---- epilogue.  Lane holds token row (lane & 31) of each token fragment
+        // and, for register v, weight-panel row (v/4)*8 + (lane/32)*4 + v%4.
+        // Results go through a per-wave LDS staging area (the stage slots are
+        // free now: 16 KiB per wave) so that global traffic is 16 bytes per lane
+        // over whole row segments.
+        uint16_t* stg = (wave < 4 ? &s_a[0][0] : &s_b[0][0]) + (wave & 3) * 8192 + opaque;
+        const int wrow0 = c_row0 + GRP * WROWS;    // first token row of this wave
+        if constexpr (EPI == EPI_STORE) {
+            // [128 rows][64 cols] bf16 (128-byte rows); 8-byte unit u of row r at u ^ ((r >> 1) & 15)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int grow = row0 + wm * WTM + i * 32 + (lane & 31);
-            if (grow >= row_end) continue;
-            if constexpr (EPI == EPI_STORE) {
-                uint16_t* out = p.out0 + static_cast<int64_t>(grow) * N;
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int c = col0 + wn * WTN + j * 32 + q * 8 + cbase;
-                        if (c < N) {
-                            uint2 v;
-                            v.x = pack2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-                            v.y = pack2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-                            *reinterpret_cast<uint2*>(out + c) = v;
+                        const int r = i * 32 + (lane & 31);
+                        const int u = j * 8 + q * 2 + (lane >> 5);
+                        uint2 v;
+                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                        *reinterpret_cast<uint2*>(stg + r * 64 + ((u ^ ((r >> 1) & 15)) << 2)) = v;
+                    }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+            for (int sidx = 0; sidx < 16; ++sidx) {
+                const int idx = sidx * 64 + lane;
+                const int r = idx >> 3, c = idx & 7;
+                const int f = (r >> 1) & 15;
+                uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (f >> 1)) << 3));
+                if (f & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+                const int grow = wrow0 + r;
+                const int gcol = c_col0 + wcol(c);
+                if (grow < c_row_end && gcol < N)
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + gcol) = v;
+            }
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            // two passes of 64 rows; per pass [64][32] bf16 arrays for A, gate, up
+            // (64-byte rows); 8-byte unit u of row r at u ^ ((r >> 2) & 7)
+            uint16_t* sA = stg;
+            uint16_t* sG = stg + 2048;
+            uint16_t* sU = stg + 4096;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = pass * 2 + ii;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = ii * 32 + (lane & 31);
+                        const int u = q * 2 + (lane >> 5);
+                        const int off = r * 32 + ((u ^ ((r >> 2) & 7)) << 2);
+                        uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
+                            ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
+                            const float g = bf2f(gb[x]);
+                            const float uu = bf2f(ub[x]);
+                            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                            ab[x] = f2bf(sg * uu);
+                        }
+                        *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                        *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                        *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int sidx = 0; sidx < 4; ++sidx) {
+                    const int idx = sidx * 64 + lane;
+                    const int r = idx >> 2, c = idx & 3;
+                    const int f = (r >> 2) & 7;
+                    const int off = r * 32 + ((c ^ (f >> 1)) << 3);
+                    uint4 va = *reinterpret_cast<const uint4*>(sA + off);
+                    uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                    uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                    if (f & 1) {
+                        va = make_uint4(va.z, va.w, va.x, va.y);
+                        vg = make_uint4(vg.z, vg.w, vg.x, vg.y);
+                        vu = make_uint4(vu.z, vu.w, vu.x, vu.y);
+                    }
+                    const int grow = wrow0 + pass * 64 + r;
+                    const int gcol = c_col0 + wq * 32 + c * 8;
+                    if (grow < c_row_end && gcol < N) {
+                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + gcol) = va;
+                        if (p.out1) {
+                            uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + gcol;
+                            *reinterpret_cast<uint4*>(h) = vg;
+                            *reinterpret_cast<uint4*>(h + N) = vu;
                         }
                     }
                 }
-            } else if constexpr (EPI == EPI_SWIGLU) {
-                constexpr int HALF = TN / 2;
-                uint16_t* a_out = p.out0 + static_cast<int64_t>(grow) * N;
-                uint16_t* h_out = p.out1 ? p.out1 + static_cast<int64_t>(grow) * (2 * N) : nullptr;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        } else {
+            // SwiGLU derivative.  Per pass of 64 rows the saved gate and up values
+            // [64][64] each (128-byte rows) are copied into the staging area with
+            // LDS-DMA; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7).  The
+            // results overwrite them in place and leave as whole row segments.
+            uint16_t* sG = stg;
+            uint16_t* sU = stg + 4096;
+            const uint32_t g_lds = lds_addr(sG), u_lds = lds_addr(sU);
+#pragma unroll   // the accumulator index must stay compile-time
+            for (int pass = 0; pass < 2; ++pass) {
+                // copy: 64 rows x 128 bytes per array = 8 DMA instructions each
+                const int prow0 = wrow0 + pass * 64;
+                const uint16_t* hbase = p.aux + static_cast<int64_t>(uni(min(prow0, c_row_end - 1))) * (2 * N) +
+                                        c_col0;
 #pragma unroll
-                for (int j = 0; j < HALF; ++j) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int c = col0 + wn * (WTN / 2) + j * 32 + q * 8 + cbase;
-                        if (c < N) {
-                            uint16_t gb[4], ub[4], ab[4];
-#pragma unroll
-                            for (int x = 0; x < 4; ++x) {
-                                gb[x] = f2bf(acc[i][j][q * 4 + x]);
-                                ub[x] = f2bf(acc[i][j + HALF][q * 4 + x]);
-                                const float g = bf2f(gb[x]);
-                                const float u = bf2f(ub[x]);
-                                const float s = g / (1.0f + __expf(-g));
-                                ab[x] = f2bf(s * u);
-                            }
-                            uint2 va, vg, vu;
-                            va.x = ab[0] | (uint32_t(ab[1]) << 16);
-                            va.y = ab[2] | (uint32_t(ab[3]) << 16);
-                            *reinterpret_cast<uint2*>(a_out + c) = va;
-                            if (h_out) {
-                                vg.x = gb[0] | (uint32_t(gb[1]) << 16);
-                                vg.y = gb[2] | (uint32_t(gb[3]) << 16);
-                                vu.x = ub[0] | (uint32_t(ub[1]) << 16);
-                                vu.y = ub[2] | (uint32_t(ub[3]) << 16);
-                                *reinterpret_cast<uint2*>(h_out + c) = vg;
-                                *reinterpret_cast<uint2*>(h_out + N + c) = vu;
-                            }
-                        }
-                    }
+                for (int d = 0; d < 8; ++d) {
+                    const int r = d * 8 + (lane >> 3);
+                    const int c = (lane & 7) ^ ((r >> 1) & 7);
+                    const int rr = min(prow0 + r, c_row_end - 1) - min(prow0, c_row_end - 1);
+                    const int cc = min(c_col0 + wcol(c), N - 8) - c_col0;
+                    const uint32_t voff = static_cast<uint32_t>((rr * 2 * N + cc) * 2);
+                    dma16(hbase, voff, g_lds + d * 1024);
+                    dma16(hbase + N, voff, u_lds + d * 1024);
                 }
-            } else {  // EPI_DSWIGLU: N == F, aux = H1 [M][2F], out0 = dH1 [M][2F]
-                const uint16_t* h1 = p.aux + static_cast<int64_t>(grow) * (2 * N);
-                uint16_t* dh = p.out0 + static_cast<int64_t>(grow) * (2 * N);
+                wait_vmcnt<0>();
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = pass * 2 + ii;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int c = col0 + wn * WTN + j * 32 + q * 8 + cbase;
-                        if (c < N) {
-                            const uint2 hg = *reinterpret_cast<const uint2*>(h1 + c);
-                            const uint2 hu = *reinterpret_cast<const uint2*>(h1 + N + c);
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = ii * 32 + (lane & 31);
+                            const int col = j * 32 + q * 8 + (lane >> 5) * 4;    // 4 columns
+                            const int off = r * 64 + (((col >> 3) ^ ((r >> 1) & 7)) << 3) + (col & 7);
+                            const uint2 hg = *reinterpret_cast<const uint2*>(sG + off);
+                            const uint2 hu = *reinterpret_cast<const uint2*>(sU + off);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
                             float dg[4], du[4];
@@ -395,23 +606,43 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 const uint32_t ubits = (x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu);
                                 const float g = bf2f(gbits);
                                 const float u = bf2f(ubits);
-                                const float da = bf2f(f2bf(acc[i][j][q * 4 + x]));
-                                const float s = 1.0f / (1.0f + __expf(-g));
-                                dg[x] = da * u * s * (1.0f + g * (1.0f - s));
-                                du[x] = da * g * s;
+                                const float da = bf2f(f2bf(acc_rd(acc[i][j][q * 4 + x])));
+                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                                dg[x] = da * u * sgm * (1.0f + g * (1.0f - sgm));
+                                du[x] = da * g * sgm;
                             }
-                            uint2 vg, vu;
-                            vg.x = pack2(dg[0], dg[1]);
-                            vg.y = pack2(dg[2], dg[3]);
-                            vu.x = pack2(du[0], du[1]);
-                            vu.y = pack2(du[2], du[3]);
-                            *reinterpret_cast<uint2*>(dh + c) = vg;
-                            *reinterpret_cast<uint2*>(dh + N + c) = vu;
+                            *reinterpret_cast<uint2*>(sG + off) =
+                                make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+                            *reinterpret_cast<uint2*>(sU + off) =
+                                make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
                         }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int sidx = 0; sidx < 8; ++sidx) {
+                    const int idx = sidx * 64 + lane;
+                    const int r = idx >> 3, c = idx & 7;
+                    const int off = r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
+                    const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                    const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                    const int grow = prow0 + r;
+                    const int gcol = c_col0 + wcol(c);
+                    if (grow < c_row_end && gcol < N) {
+                        uint16_t* dh = p.out0 + static_cast<int64_t>(grow) * (2 * N) + gcol;
+                        *reinterpret_cast<uint4*>(dh) = vg;
+                        *reinterpret_cast<uint4*>(dh + N) = vu;
                     }
                 }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
         }
+        };
+        // Each group runs its own copy of the K loop and the epilogue, so its
+        // accumulators never have to be merged with the other group's path.
+        if (grp == 0) run_group(GrpTag<0>{}); else run_group(GrpTag<1>{});
+
+        // every wave is done with the staging area before the next tile's copies
+        block_barrier();
     }
 }
 
@@ -424,32 +655,32 @@ __global__ void round_bf16_kernel(const float* __restrict__ in, uint16_t* __rest
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool W_KN, int EPI>
+template <bool W_KN, int EPI>
 static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream) {
-    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int64_t tiles_n = (p.N + TILE_COLS - 1) / TILE_COLS;
-    // Upper bound of sum_e ceil(m_e / BM) without reading the offsets.
-    const int64_t tiles_m_max = (static_cast<int64_t>(p.M) + static_cast<int64_t>(p.E) * (BM - 1)) / BM;
+    // Upper bound of sum_e ceil(m_e / TBM) without reading the offsets.
+    const int64_t tiles_m_max = (static_cast<int64_t>(p.M) + static_cast<int64_t>(p.E) * (TBM - 1)) / TBM;
     const int64_t upper = tiles_m_max * tiles_n;
     int64_t grid = num_cu;            // one workgroup per CU (LDS-limited)
     if (upper < grid) grid = upper;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WAVES_M, WAVES_N, W_KN, EPI>),
-                       dim3(static_cast<unsigned>(grid)), dim3(WAVES_M * WAVES_N * 64), 0, stream, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<W_KN, EPI>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<256, 256, 2, 4, false, EPI_SWIGLU>(p, num_cu, s);
+    return launch_cfg<false, EPI_SWIGLU>(p, num_cu, s);
 }
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<256, 256, 2, 4, false, EPI_STORE>(p, num_cu, s);
+    return launch_cfg<false, EPI_STORE>(p, num_cu, s);
 }
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<256, 256, 2, 4, true, EPI_DSWIGLU>(p, num_cu, s);
+    return launch_cfg<true, EPI_DSWIGLU>(p, num_cu, s);
 }
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<256, 256, 2, 4, true, EPI_STORE>(p, num_cu, s);
+    return launch_cfg<true, EPI_STORE>(p, num_cu, s);
 }
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
