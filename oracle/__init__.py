@@ -55,8 +55,12 @@ def _load():
                 getattr(lib, name).argtypes = [i64, i64, i64, p, p, p, p, p, p, p]
             for name in ("oracle_dgrad_f32", "oracle_dgrad_f64"):
                 getattr(lib, name).argtypes = [i64, i64, i64, p, p, p, p, p, p, p]
+            lib.oracle_swiglu_f32.argtypes = [i64, i64, p, p, p]
+            lib.oracle_fc2_f32.argtypes = [i64, i64, i64, p, p, p, p]
+            lib.oracle_dgrad_fc1_f32.argtypes = [i64, i64, i64, p, p, p, p]
             for name in ("oracle_round_bf16", "oracle_forward_f32", "oracle_forward_f64",
-                         "oracle_dgrad_f32", "oracle_dgrad_f64"):
+                         "oracle_dgrad_f32", "oracle_dgrad_f64", "oracle_swiglu_f32", "oracle_fc2_f32",
+                         "oracle_dgrad_fc1_f32"):
                 getattr(lib, name).restype = None
             _lib = lib
     return _lib
@@ -148,6 +152,42 @@ def dgrad(dy, h1, offsets, w1, w2):
     _load().oracle_dgrad_f32(E, H, F, _ptr(off), _ptr(dy32), _ptr(h132), _ptr(w132),
                              _ptr(w232), _ptr(dh1), _ptr(dx))
     return {"dh1": dh1, "dx": dx}
+
+
+def swiglu(h1, offsets):
+    """SwiGLU alone from a given H1 [M,2F] (bf16 values): a [M,F]."""
+    h132 = _as_f32(h1)
+    M, twoF = h132.shape
+    F = twoF // 2
+    off = _check_offsets(offsets, np.asarray(offsets).shape[0] - 1, M)
+    a = np.full((M, F), np.nan, np.float32)
+    _load().oracle_swiglu_f32(off.shape[0] - 1, F, _ptr(off), _ptr(h132), _ptr(a))
+    return a
+
+
+def fc2(a, offsets, w2):
+    """FC2 alone from a given A [M,F] (bf16 values): y [M,H] (fp32 holding bf16)."""
+    a32, w232 = _as_f32(a), _as_f32(w2)
+    E, H, F = w232.shape
+    M = a32.shape[0]
+    assert a32.shape == (M, F)
+    off = _check_offsets(offsets, E, M)
+    y = np.full((M, H), np.nan, np.float32)
+    _load().oracle_fc2_f32(E, H, F, _ptr(off), _ptr(a32), _ptr(w232), _ptr(y))
+    return y
+
+
+def dgrad_fc1(dh1, offsets, w1):
+    """Last step of the input gradient alone, from a given dH1 [M,2F]: dx [M,H]."""
+    dh132, w132 = _as_f32(dh1), _as_f32(w1)
+    E, twoF, H = w132.shape
+    F = twoF // 2
+    M = dh132.shape[0]
+    assert dh132.shape == (M, 2 * F)
+    off = _check_offsets(offsets, E, M)
+    dx = np.full((M, H), np.nan, np.float32)
+    _load().oracle_dgrad_fc1_f32(E, H, F, _ptr(off), _ptr(dh132), _ptr(w132), _ptr(dx))
+    return dx
 
 
 def forward64(x, offsets, w1, w2):

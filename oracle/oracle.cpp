@@ -66,13 +66,24 @@ template <> double rnd<double>(double v) { return v; }
 template <typename T> T sigmoid(T g) { return T(1) / (T(1) + std::exp(-g)); }
 template <typename T> T silu(T g) { return g / (T(1) + std::exp(-g)); }
 
-// Forward for one routed row r of expert e.
+// SwiGLU for one routed row r: A[r, j] = silu(gate) * up with gate = H1[r, j],
+// up = H1[r, F + j] (the rounded H1 values).
 template <typename T>
-void forward_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, const T* w2e,
-                 T* h1, T* a, T* y) {
+void swiglu_row(int64_t r, int64_t F, const T* h1, T* a) {
+    const T* h1r = h1 + r * 2 * F;
+    T* ar = a + r * F;
+    for (int64_t j = 0; j < F; ++j) {
+        const T g = h1r[j];
+        const T u = h1r[F + j];
+        ar[j] = rnd<T>(silu<T>(g) * u);
+    }
+}
+
+// FC1 + SwiGLU for one routed row r of expert e: H1 row and A row.
+template <typename T>
+void fc1_swiglu_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, T* h1, T* a) {
     const T* xr = x + r * H;
     T* h1r = h1 + r * 2 * F;
-    T* ar = a + r * F;
     // FC1: H1[r, j] = sum_k X[r, k] * W1_e[j, k]
     for (int64_t j = 0; j < 2 * F; ++j) {
         const T* wj = w1e + j * H;
@@ -80,13 +91,13 @@ void forward_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, cons
         for (int64_t k = 0; k < H; ++k) acc += xr[k] * wj[k];
         h1r[j] = rnd<T>(acc);
     }
-    // SwiGLU: A[r, j] = silu(gate) * up, gate = H1[r, j], up = H1[r, F + j]
-    for (int64_t j = 0; j < F; ++j) {
-        const T g = h1r[j];
-        const T u = h1r[F + j];
-        ar[j] = rnd<T>(silu<T>(g) * u);
-    }
-    // FC2: Y[r, n] = sum_j A[r, j] * W2_e[n, j]
+    swiglu_row<T>(r, F, h1, a);
+}
+
+// FC2 for one routed row r of expert e: Y[r, n] = sum_j A[r, j] * W2_e[n, j].
+template <typename T>
+void fc2_row(int64_t r, int64_t H, int64_t F, const T* a, const T* w2e, T* y) {
+    const T* ar = a + r * F;
     T* yr = y + r * H;
     for (int64_t n = 0; n < H; ++n) {
         const T* wn = w2e + n * F;
@@ -96,11 +107,19 @@ void forward_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, cons
     }
 }
 
-// Input gradient for one routed row r of expert e.  acc is scratch of
-// max(F, H) elements.
+// Forward for one routed row r of expert e.
 template <typename T>
-void dgrad_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const T* w1e,
-               const T* w2e, T* dh1, T* dx, T* acc) {
+void forward_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, const T* w2e,
+                 T* h1, T* a, T* y) {
+    fc1_swiglu_row<T>(r, H, F, x, w1e, h1, a);
+    fc2_row<T>(r, H, F, a, w2e, y);
+}
+
+// dA and the SwiGLU derivative for one routed row r of expert e -> dH1 row.
+// acc is scratch of F elements.
+template <typename T>
+void dswiglu_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const T* w2e, T* dh1,
+                 T* acc) {
     const T* dyr = dy + r * H;
     const T* h1r = h1 + r * 2 * F;
     T* dh1r = dh1 + r * 2 * F;
@@ -122,7 +141,13 @@ void dgrad_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const 
         dh1r[j] = rnd<T>(da * u * s * (T(1) + g * (T(1) - s)));
         dh1r[F + j] = rnd<T>(da * g * s);
     }
-    // dX[r, k] = sum_j dH1[r, j] * W1_e[j, k], j in increasing order.
+}
+
+// dX for one routed row r of expert e: dX[r, k] = sum_j dH1[r, j] * W1_e[j, k],
+// j in increasing order.  acc is scratch of H elements.
+template <typename T>
+void dgrad_fc1_row(int64_t r, int64_t H, int64_t F, const T* dh1, const T* w1e, T* dx, T* acc) {
+    const T* dh1r = dh1 + r * 2 * F;
     for (int64_t k = 0; k < H; ++k) acc[k] = 0;
     for (int64_t j = 0; j < 2 * F; ++j) {
         const T d = dh1r[j];
@@ -131,6 +156,15 @@ void dgrad_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const 
     }
     T* dxr = dx + r * H;
     for (int64_t k = 0; k < H; ++k) dxr[k] = rnd<T>(acc[k]);
+}
+
+// Input gradient for one routed row r of expert e.  acc is scratch of
+// max(F, H) elements.
+template <typename T>
+void dgrad_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const T* w1e,
+               const T* w2e, T* dh1, T* dx, T* acc) {
+    dswiglu_row<T>(r, H, F, dy, h1, w2e, dh1, acc);
+    dgrad_fc1_row<T>(r, H, F, dh1, w1e, dx, acc);
 }
 
 template <typename T>
@@ -161,9 +195,51 @@ void dgrad_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* dy,
     }
 }
 
+template <typename T>
+void fc2_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* a, const T* w2, T* y) {
+    for (int64_t e = 0; e < E; ++e) {
+        const T* w2e = w2 + e * H * F;
+#pragma omp parallel for schedule(static)
+        for (int64_t r = off[e]; r < off[e + 1]; ++r) fc2_row<T>(r, H, F, a, w2e, y);
+    }
+}
+
+template <typename T>
+void dgrad_fc1_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* dh1, const T* w1,
+                   T* dx) {
+    for (int64_t e = 0; e < E; ++e) {
+        const T* w1e = w1 + e * 2 * F * H;
+#pragma omp parallel
+        {
+            std::vector<T> acc(H);
+#pragma omp for schedule(static)
+            for (int64_t r = off[e]; r < off[e + 1]; ++r) dgrad_fc1_row<T>(r, H, F, dh1, w1e, dx, acc.data());
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// SwiGLU alone, from a given H1 [M][2F] -> a [M][F], rows [offsets[0], offsets[E]).
+void oracle_swiglu_f32(int64_t E, int64_t F, const int64_t* offsets, const float* h1, float* a) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = offsets[0]; r < offsets[E]; ++r) swiglu_row<float>(r, F, h1, a);
+}
+
+// FC2 alone (the second step of the forward), from a given A [M][F] -> y [M][H].
+void oracle_fc2_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets, const float* a,
+                    const float* w2, float* y) {
+    fc2_all<float>(E, H, F, offsets, a, w2, y);
+}
+
+// The last step of the input gradient alone, from a given dH1 [M][2F] -> dx [M][H].
+void oracle_dgrad_fc1_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
+                          const float* dh1, const float* w1, float* dx) {
+    dgrad_fc1_all<float>(E, H, F, offsets, dh1, w1, dx);
+}
+
 
 // bf16 rounding of n fp32 values (exposed so the tests can pin it).
 void oracle_round_bf16(const float* in, float* out, int64_t n) {

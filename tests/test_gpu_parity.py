@@ -10,7 +10,7 @@ import torch
 import oracle
 import workload
 from gpu_harness import DeviceCase, log
-from parity import check
+from parity import DH1_ELEM_REL, check, check_chained, stagewise
 
 pytestmark = pytest.mark.gpu
 
@@ -20,30 +20,27 @@ def _gpu_ok():
         pytest.skip("no GPU")
 
 
-def run_full_parity(case, check_dgrad_with_oracle_h1=True):
-    """Whole-problem parity (every element)."""
+def run_full_parity(case):
+    """Whole-problem parity (every element), stage by stage."""
     _gpu_ok()
     log(f"[parity] {case.name} E={case.E} H={case.H} F={case.F} M={case.M} counts={list(case.counts)[:16]}")
     dc = DeviceCase(case)
     h1, a, y = dc.forward()
+    ws, dx = dc.dgrad(h1)
     torch.cuda.synchronize()
-    ref = oracle.forward(case.x, case.offsets, case.w1, case.w2)
     rows = np.arange(int(case.offsets[0]), int(case.offsets[-1]))
-    out = [check("h1", h1, ref["h1"], rows), check("a", a, ref["a"], rows), check("y", y, ref["y"], rows)]
-    # dgrad from the same saved H1 on both sides (the oracle's), then end to end
-    if check_dgrad_with_oracle_h1:
-        h1_ref = torch.from_numpy(ref["h1"]).to(torch.bfloat16).to(dc.dev)
-        ws, dx = dc.dgrad(h1_ref)
-        torch.cuda.synchronize()
-        dref = oracle.dgrad(case.dy, ref["h1"], case.offsets, case.w1, case.w2)
-        out += [check("dh1", ws, dref["dh1"], rows), check("dx", dx, dref["dx"], rows)]
-    ws2, dx2 = dc.dgrad(h1)
+    out = stagewise(case.x, case.dy, case.offsets, case.w1, case.w2, h1, a, y, ws, dx, rows)
+    # dgrad from the oracle's H1 as well (same saved activation on both sides)
+    ref = oracle.forward(case.x, case.offsets, case.w1, case.w2)
+    h1_ref = torch.from_numpy(ref["h1"]).to(torch.bfloat16).to(dc.dev)
+    ws_o, dx_o = dc.dgrad(h1_ref)
     torch.cuda.synchronize()
-    dref2 = oracle.dgrad(case.dy, h1.cpu(), case.offsets, case.w1, case.w2)
-    out += [check("dx_e2e", dx2, dref2["dx"], rows)]
+    dref = oracle.dgrad(case.dy, ref["h1"], case.offsets, case.w1, case.w2)
+    out += [check("dh1_from_oracle_h1", ws_o, dref["dh1"], rows, elem_rel=DH1_ELEM_REL),
+            check_chained("dx_from_oracle_h1", dx_o, dref["dx"], rows)]
     log(f"[parity] {case.name} ok: " + ", ".join(f"{o['name']} rl2={o.get('rel_l2', 0):.2e} "
                                                   f"wr={o.get('worst_ratio', 0):.2f}" for o in out))
-    return dc, (h1, a, y, dx2)
+    return dc, (h1, a, y, dx)
 
 
 def test_device_bf16_rounding_exhaustive():
@@ -243,16 +240,13 @@ def test_workload_sampled_rows(name):
     torch.cuda.synchronize()
     rows = _sampled_rows(case)
     log(f"[sampled] {name}: oracle on {rows.size} rows")
-    expert, compact = oracle.sample_rows(case.offsets, rows)
-    xs = case.x[torch.from_numpy(rows)]
-    ref = oracle.forward(xs, compact, case.w1, case.w2)
-    check("h1", h1[torch.from_numpy(rows).cuda()], ref["h1"])
-    check("y", y[torch.from_numpy(rows).cuda()], ref["y"])
-    h1s = h1[torch.from_numpy(rows).cuda()].cpu()
-    dys = case.dy[torch.from_numpy(rows)]
-    dref = oracle.dgrad(dys, h1s, compact, case.w1, case.w2)
-    check("dh1", ws[torch.from_numpy(rows).cuda()], dref["dh1"])
-    check("dx", dx[torch.from_numpy(rows).cuda()], dref["dx"])
+    _, compact = oracle.sample_rows(case.offsets, rows)
+    rt = torch.from_numpy(rows)
+    rd = rt.to(dc.dev)
+    out = stagewise(case.x[rt], case.dy[rt], compact, case.w1, case.w2,
+                    h1[rd], a[rd], y[rd], ws[rd], dx[rd])
+    log(f"[sampled] {name} ok: " + ", ".join(f"{o['name']} rl2={o.get('rel_l2', 0):.2e} "
+                                             f"wr={o.get('worst_ratio', 0):.2f}" for o in out))
     # padding rows (if any) are exact zeros everywhere
     for e in range(case.E):
         pad = slice(int(case.offsets[e] + case.counts[e]), int(case.offsets[e + 1]))

@@ -388,3 +388,13 @@ def test_tiny_workload_golden():
     from golden.make_golden import summarize
     now = summarize()
     assert now == gold
+
+
+def test_stage_entry_points_compose_to_the_whole_passes():
+    """swiglu(H1), fc2(A) and dgrad_fc1(dH1) are the later steps of forward / dgrad (bitwise)."""
+    c, x, w1, w2, dy = _random_problem([5, 0, 7, 3], 24, 16, 29, w_std=0.3)
+    fw = oracle.forward(x, c.offsets, w1, w2)
+    np.testing.assert_array_equal(oracle.swiglu(fw["h1"], c.offsets), fw["a"])
+    np.testing.assert_array_equal(oracle.fc2(fw["a"], c.offsets, w2), fw["y"])
+    dg = oracle.dgrad(dy, fw["h1"], c.offsets, w1, w2)
+    np.testing.assert_array_equal(oracle.dgrad_fc1(dg["dh1"], c.offsets, w1), dg["dx"])
