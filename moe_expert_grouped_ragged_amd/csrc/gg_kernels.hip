@@ -50,7 +50,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 #define GG_AS3(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int BK = 32;  // K elements per pipeline stage
+constexpr int BK = 64;  // K elements per pipeline stage (128-byte rows of a K-contiguous panel)
+constexpr int HK = 32;  // K elements per ping-pong phase (half a stage)
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -63,20 +64,20 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // Chunk swizzles (chosen from LDS bank-conflict counter measurements on
-// gfx950).  K-contiguous panels are [row][32 k] (64-byte rows, four 16-byte
-// chunks); chunk c of row r is stored at c ^ kswz(r), which keeps the
-// 16-byte fragment reads (32 rows x 2 chunks per wave) conflict-free.
-// N-contiguous panels are [32 k][BN n]; chunk c of row k is stored at
-// c ^ nswz(k), which keeps the 8-byte transpose reads conflict-free (it
-// permutes 4-chunk blocks, so column offsets of 16 chunks stay additive).
-__device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+// gfx950).  K-contiguous panels are [row][64 k] (128-byte rows, eight 16-byte
+// chunks); chunk c of row r is stored at c ^ kswz(r), which keeps the 16-byte
+// fragment reads (32 rows x 2 chunks per wave) conflict-free.  N-contiguous
+// panels are [64 k][BN n]; chunk c of row k is stored at c ^ nswz(k), which
+// keeps the 8-byte transpose reads conflict-free (it permutes 4-chunk blocks,
+// so column offsets of 16 chunks stay additive).
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int nswz(int k) { return (k & 3) << 2; }
 
-// [row][32] K-contiguous panel: element offset of logical 16-byte chunk c (0..3) of `row`.
+// [row][64] K-contiguous panel: element offset of logical 16-byte chunk c (0..7) of `row`.
 __device__ __forceinline__ int kc_off(int row, int c) {
     return row * BK + ((c ^ kswz(row)) << 3);
 }
-// [32][BN] N-contiguous panel: element offset of column n (multiple of 4) in row k.
+// [64][BN] N-contiguous panel: element offset of column n (multiple of 4) in row k.
 template <int BN>
 __device__ __forceinline__ int nc_off(int k, int n) {
     return k * BN + (((n >> 3) ^ nswz(k)) << 3) + (n & 7);
@@ -90,8 +91,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
     asm volatile("" ::: "memory");
 }
+// Workgroup barrier for the copy pipeline.  It first waits for this wave's
+// outstanding LDS operations: a fragment read issued before the barrier must
+// have completed before another wave refills that stage slot with LDS-DMA.
+// (Outstanding HBM->LDS copies are waited for explicitly with wait_vmcnt.)
 __device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -182,7 +187,7 @@ __device__ __forceinline__ int find_expert(const int* s_pre, int E, int t) {
 // that stage from LDS and issues the HBM->LDS copies, and a barrier swaps the
 // roles, so the matrix pipe of every SIMD always has a wave feeding it.
 template <int V> struct GrpTag { static constexpr int value = V; };
-constexpr int TBM = 256, TBN = 256, NWAVES = 8, NTHREADS = NWAVES * 64, NSTAGE = 4;
+constexpr int TBM = 256, TBN = 256, NWAVES = 8, NTHREADS = NWAVES * 64, NSTAGE = 2;
 constexpr int WROWS = 128, WCOLS = 64, FM = WROWS / 32, FN = WCOLS / 32;
 constexpr int A_STAGE = TBM * BK, B_STAGE = TBN * BK;          // elements per stage
 constexpr int A_PW = A_STAGE * 2 / 1024 / NWAVES;               // 1 KiB DMA instructions per wave
@@ -243,8 +248,8 @@ void grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int i = 0; i < A_PW; ++i) {
             const int pos = (wave * A_PW + i) * 64 + lane;   // 16-byte chunk slot in the stage
-            const int r = pos >> 2;
-            const int c = (pos & 3) ^ kswz(r);                 // logical chunk stored there
+            const int r = pos >> 3;
+            const int c = (pos & 7) ^ kswz(r);                 // logical chunk stored there
             a_voff[i] = static_cast<uint32_t>((min(r, rows - 1) * K + c * 8) * 2);
             a_kc[i] = c * 8;
         }
@@ -252,8 +257,8 @@ void grouped_gemm_kernel(const GemmParams p) {
         for (int i = 0; i < B_PW; ++i) {
             const int pos = (wave * B_PW + i) * 64 + lane;
             if constexpr (!W_KN) {
-                const int r = pos >> 2;
-                const int c = (pos & 3) ^ kswz(r);
+                const int r = pos >> 3;
+                const int c = (pos & 7) ^ kswz(r);
                 int wrow;
                 if constexpr (EPI == EPI_SWIGLU) {
                     const int half = r / (TBN / 2);
@@ -316,23 +321,21 @@ void grouped_gemm_kernel(const GemmParams p) {
     // stages it has in flight.
     auto wait_stage = [&](int newer) {
         if (newer <= 0) wait_vmcnt<0>();
-        else if (newer == 1) wait_vmcnt<LPS>();
-        else if (newer == 2) wait_vmcnt<2 * LPS>();
-        else wait_vmcnt<3 * LPS>();
+        else wait_vmcnt<LPS>();
     };
 
     // Zero the K positions >= K of a stage (only when K % BK != 0, last stage).
     auto zero_tail = [&](int kt) {
         const int stage = kt % NSTAGE;
         const int k0 = kt * BK;
-        for (int idx = tid; idx < TBM * 4; idx += NTHREADS) {
-            const int r = idx >> 2, c = idx & 3;
+        for (int idx = tid; idx < TBM * 8; idx += NTHREADS) {
+            const int r = idx >> 3, c = idx & 7;
             if (k0 + c * 8 >= K)
                 *reinterpret_cast<uint4*>(&s_a[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
         }
         if constexpr (!W_KN) {
-            for (int idx = tid; idx < TBN * 4; idx += NTHREADS) {
-                const int r = idx >> 2, c = idx & 3;
+            for (int idx = tid; idx < TBN * 8; idx += NTHREADS) {
+                const int r = idx >> 3, c = idx & 7;
                 if (k0 + c * 8 >= K)
                     *reinterpret_cast<uint4*>(&s_b[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
             }
@@ -359,12 +362,14 @@ void grouped_gemm_kernel(const GemmParams p) {
     };
 
     bf16x8 fa[2][FM], fb[2][FN];
-    auto load_frags = [&](int kt) {
-        const uint16_t* sa = s_a[kt % NSTAGE];
-        const uint16_t* sb = s_b[kt % NSTAGE];
+    // fragments of half-stage h (K elements h*32 .. h*32+31): stage h/2, half h%2
+    auto load_frags = [&](int h) {
+        const uint16_t* sa = s_a[(h >> 1) % NSTAGE];
+        const uint16_t* sb = s_b[(h >> 1) % NSTAGE];
+        const int half = h & 1;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
-            const int ch = ss * 2 + (lane >> 5);
+            const int ch = half * 4 + ss * 2 + (lane >> 5);
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int r = grp * WROWS + i * 32 + (lane & 31);
@@ -379,7 +384,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                     // lane 16g + 4s + q supplies (k = kb + s, n = nb + 4q) and receives
                     // column nb + (lane & 15), rows kb .. kb+3 (ds_read_b64_tr_b16).
                     const int g = lane >> 4;
-                    const int kb = ss * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
+                    const int kb = half * HK + ss * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
                     const int n = wfrag(j) + 16 * (g & 1) + 4 * (lane & 3);
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
@@ -417,16 +422,21 @@ void grouped_gemm_kernel(const GemmParams p) {
             zero_tail(0);
             __syncthreads();
         }
-        // The two groups run the same barrier sequence (two per K stage) on
-        // separate code paths so that each keeps its fragments in fixed registers.
-        auto mid_stage = [&](int kt) {
-            if (kt + 1 < kiters) wait_stage(min(NSTAGE - 2, kiters - 2 - kt));   // stage kt+1 landed
+        // Phases are half-stages.  The two groups run the same barrier sequence
+        // (two per phase) on separate code paths so that each keeps its
+        // fragments in fixed registers.
+        const int nh = 2 * kiters;
+        auto mid_phase = [&](int h) {
+            // half h+1 starts a new stage: it must have landed (nothing newer is in flight)
+            if ((h & 1) && h + 1 < nh) wait_stage(0);
             block_barrier();
-            // stage kt is consumed by both groups: refill its slot
-            if (kt + NSTAGE < kiters) issue(kt + NSTAGE);
-            if (k_tail && kt + 1 == kiters - 1) {
-                zero_tail(kt + 1);
-                __syncthreads();
+            if (h & 1) {
+                // stage h/2 is consumed by both groups: refill its slot
+                if ((h >> 1) + NSTAGE < kiters) issue((h >> 1) + NSTAGE);
+                if (k_tail && (h + 1) / 2 == kiters - 1 && h + 1 < nh) {
+                    zero_tail(kiters - 1);
+                    __syncthreads();
+                }
             }
         };
         auto run_group = [&](auto gtag) {
@@ -439,22 +449,22 @@ void grouped_gemm_kernel(const GemmParams p) {
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
         if constexpr (GRP == 0) {
             load_frags(0);
-            for (int kt = 0; kt < kiters; ++kt) {
+            for (int h = 0; h < nh; ++h) {
                 __builtin_amdgcn_sched_barrier(0);
-                mma();                                   // phase 0: compute stage kt
+                mma();                                   // phase 0: compute half h
                 __builtin_amdgcn_sched_barrier(0);
-                mid_stage(kt);
-                if (kt + 1 < kiters) load_frags(kt + 1); // phase 1: read stage kt+1
+                mid_phase(h);
+                if (h + 1 < nh) load_frags(h + 1);       // phase 1: read half h+1
                 __builtin_amdgcn_sched_barrier(0);
                 block_barrier();
             }
         } else {
-            for (int kt = 0; kt < kiters; ++kt) {
+            for (int h = 0; h < nh; ++h) {
                 __builtin_amdgcn_sched_barrier(0);
-                load_frags(kt);                          // phase 0: read stage kt
+                load_frags(h);                           // phase 0: read half h
                 __builtin_amdgcn_sched_barrier(0);
-                mid_stage(kt);
-                mma();                                   // phase 1: compute stage kt
+                mid_phase(h);
+                mma();                                   // phase 1: compute half h
                 __builtin_amdgcn_sched_barrier(0);
                 block_barrier();
             }
