@@ -71,6 +71,8 @@ def cpu_baseline(case, target_s: float):
 
     import oracle
     threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
     oracle.set_threads(threads)
     w1 = oracle._as_f32(case.w1)
     w2 = oracle._as_f32(case.w2)
@@ -87,10 +89,15 @@ def cpu_baseline(case, target_s: float):
         oracle.dgrad(dys, fw["h1"], comp, w1, w2)
         return rows.size, time.perf_counter() - t0
 
-    n, t = run(4)
-    per_row = t / max(n, 1)
-    k = max(4, int(target_s / max(per_row * len(live), 1e-9)))
-    n, t = run(k)
+    # grow the sample until one run takes about target_s (small samples
+    # under-use the threads, so a single extrapolation undershoots)
+    cap = int(np.max(np.diff(off)))
+    k = 4
+    while True:
+        n, t = run(k)
+        if t >= 0.6 * target_s or k >= cap:
+            break
+        k = min(cap, max(k + 1, int(k * min(8.0, 0.9 * target_s / max(t, 1e-3)))))
     flops = 12.0 * n * case.H * case.F
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {k} rows of each of the {len(live)} non-empty experts ({n} routed rows "
@@ -106,6 +113,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB five times "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -115,6 +125,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
 
     import workload
     import moe_expert_grouped_ragged_amd as gg
