@@ -46,7 +46,8 @@
  *    GPU/library pairs fail explicitly, TE device-metadata pull request,
  *    "Summary").  Launch failures give GG_ERR_HIP.
  *  - Limits: 1 <= E <= GG_MAX_EXPERTS; H and F positive multiples of 8;
- *    M < 2^31.
+ *    H < 2^22 and 2F < 2^22; one expert's W1 below 2 GiB (4*F*H < 2^31
+ *    bytes); M < 2^31.
  */
 #ifndef GG_H_
 #define GG_H_

@@ -66,7 +66,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(int64_t M, int64_t E, int64_t H, int64_t F) {
     if (E < 1 || E > GG_MAX_EXPERTS) return GG_ERR_INVALID_ARGUMENT;
     if (H <= 0 || F <= 0 || (H % 8) != 0 || (F % 8) != 0) return GG_ERR_INVALID_ARGUMENT;
-    if (H > (int64_t(1) << 24) || F > (int64_t(1) << 24)) return GG_ERR_INVALID_ARGUMENT;
+    // the kernels address one expert's weight matrix and a 256-row token panel
+    // with 32-bit byte offsets
+    if (H >= (int64_t(1) << 22) || 2 * F >= (int64_t(1) << 22)) return GG_ERR_INVALID_ARGUMENT;
+    if (4 * F * H >= (int64_t(1) << 31)) return GG_ERR_INVALID_ARGUMENT;
     if (M < 0 || M >= (int64_t(1) << 31)) return GG_ERR_INVALID_ARGUMENT;
     return GG_OK;
 }

@@ -96,9 +96,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // have completed before another wave refills that stage slot with LDS-DMA.
 // (Outstanding HBM->LDS copies are waited for explicitly with wait_vmcnt.)
 __device__ __forceinline__ void block_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); the builtin keeps the compiler's count in step
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ const T* uni_ptr(const T* ptr) {
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // One wave-wide LDS-DMA load: every lane copies 16 bytes from base + voff
@@ -111,11 +120,9 @@ __device__ __forceinline__ void block_barrier() {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+                 :: "v"(voff), "s"(uni_ptr(base)), "s"(uni(lds)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
-
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Read one accumulator register in the epilogue.  The accumulators live in
 // AGPRs; reading them one at a time where they are consumed keeps the
@@ -132,9 +139,18 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>(GG_AS3(const_cast<T*>(p)))));
 }
 
+// Experts with at most SMALL_M rows take the weight-streaming flavor: one work
+// item per block of output columns covering all of the expert's rows, so each
+// weight byte is read once per pass.  Larger experts are cut into 256-row tiles.
+constexpr int SMALL_M = 64;
+
+// Per-expert work counts and their exclusive prefix sums in LDS, for both
+// flavors: s_pre counts 256x256 tiles of the large experts, s_spre counts
+// streaming items of the small ones.  Offsets are clamped into [0, M] so that
+// bad offsets cannot index out of bounds.
 template <int NT>
-__device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M,
-                                               int bm, int tiles_n, int* s_off, int* s_pre) {
+__device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M, int bm,
+                                               int tiles_n, int items_n, int* s_off, int* s_pre, int* s_spre) {
     const int tid = threadIdx.x;
     for (int e = tid; e <= E; e += NT) {
         int64_t o = offsets[e];
@@ -147,24 +163,40 @@ __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offse
         const int per = (E + 63) / 64;
         const int e0 = lane * per;
         const int e1 = min(E, e0 + per);
-        int sum = 0;
-        for (int e = e0; e < e1; ++e) {
+        auto big = [&](int e) {
             const int m = max(0, s_off[e + 1] - s_off[e]);
-            sum += ((m + bm - 1) / bm) * tiles_n;
+            return m > SMALL_M ? ((m + bm - 1) / bm) * tiles_n : 0;
+        };
+        auto small = [&](int e) {
+            const int m = max(0, s_off[e + 1] - s_off[e]);
+            return (m > 0 && m <= SMALL_M) ? items_n : 0;
+        };
+        int sum = 0, ssum = 0;
+        for (int e = e0; e < e1; ++e) {
+            sum += big(e);
+            ssum += small(e);
         }
-        int incl = sum;
+        int incl = sum, sincl = ssum;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
+            const int sv = __shfl_up(sincl, d, 64);
+            if (lane >= d) {
+                incl += v;
+                sincl += sv;
+            }
         }
-        int run = incl - sum;
+        int run = incl - sum, srun = sincl - ssum;
         for (int e = e0; e < e1; ++e) {
             s_pre[e] = run;
-            const int m = max(0, s_off[e + 1] - s_off[e]);
-            run += ((m + bm - 1) / bm) * tiles_n;
+            s_spre[e] = srun;
+            run += big(e);
+            srun += small(e);
         }
-        if (lane == 63) s_pre[E] = incl;
+        if (lane == 63) {
+            s_pre[E] = incl;
+            s_spre[E] = sincl;
+        }
     }
     __syncthreads();
 }
@@ -198,16 +230,25 @@ static_assert(A_PW * NWAVES * 1024 == A_STAGE * 2 && B_PW * NWAVES * 1024 == B_S
 template <bool W_KN, int EPI>
 __global__ __launch_bounds__(NTHREADS)
 void grouped_gemm_kernel(const GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s_a[NSTAGE][A_STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_b[NSTAGE][B_STAGE];
+    // Operand stages: NSTAGE token panels, then NSTAGE weight panels (the
+    // streaming flavor lays its own stages over the same bytes).
+    __shared__ __attribute__((aligned(1024))) uint16_t s_buf[NSTAGE * (A_STAGE + B_STAGE)];
     __shared__ int s_off[GG_KMAX_EXPERTS + 1];
     __shared__ int s_pre[GG_KMAX_EXPERTS + 1];
+    __shared__ int s_spre[GG_KMAX_EXPERTS + 1];
+    auto s_a = [&](int st) -> uint16_t* { return s_buf + st * A_STAGE; };
+    auto s_b = [&](int st) -> uint16_t* { return s_buf + NSTAGE * A_STAGE + st * B_STAGE; };
 
     const int E = p.E, M = p.M, K = p.K, N = p.N;
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int tiles_n = (N + TILE_COLS - 1) / TILE_COLS;
-    build_schedule<NTHREADS>(p.offsets, E, M, TBM, tiles_n, s_off, s_pre);
-    const int total = s_pre[E];
+    // streaming flavor: an item is all rows of one small expert x S_COLS output
+    // columns (256 weight rows: for SwiGLU 128 gate rows and the matching 128 up rows)
+    constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 128 : 256;
+    const int items_n = (N + S_COLS - 1) / S_COLS;
+    build_schedule<NTHREADS>(p.offsets, E, M, TBM, tiles_n, items_n, s_off, s_pre, s_spre);
+    const int n_stream = uni(s_spre[E]);
+    const int total = n_stream + uni(s_pre[E]);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -216,8 +257,8 @@ void grouped_gemm_kernel(const GemmParams p) {
     const int wq = wave & 3;            // weight-row block
     const int kiters = (K + BK - 1) / BK;
     const bool k_tail = (K % BK) != 0;
-    const uint32_t a_lds0 = lds_addr(&s_a[0][0]) + wave * A_PW * 1024;
-    const uint32_t b_lds0 = lds_addr(&s_b[0][0]) + wave * B_PW * 1024;
+    const uint32_t a_lds0 = lds_addr(s_a(0)) + wave * A_PW * 1024;
+    const uint32_t b_lds0 = lds_addr(s_b(0)) + wave * B_PW * 1024;
 
     // Workgroups are dealt round-robin over the 8 XCDs; give the workgroups of
     // one XCD consecutive tiles so that tiles sharing panels share an L2.
@@ -234,7 +275,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     int a_kc[A_PW];                   // k offset of the chunk (K-contiguous)
     int b_kc[B_PW];                   // k offset (K-contiguous) / panel row (N-contiguous)
 
-    auto setup_tile = [&](int t) {
+    auto setup_tile = [&](int t) {   // t: index among the 256x256 tiles
         const int e = uni(find_expert(s_pre, E, t));
         const int local = t - uni(s_pre[e]);
         const int rb = uni(s_off[e]);
@@ -331,19 +372,19 @@ void grouped_gemm_kernel(const GemmParams p) {
         for (int idx = tid; idx < TBM * 8; idx += NTHREADS) {
             const int r = idx >> 3, c = idx & 7;
             if (k0 + c * 8 >= K)
-                *reinterpret_cast<uint4*>(&s_a[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(s_a(stage) + kc_off(r, c)) = make_uint4(0, 0, 0, 0);
         }
         if constexpr (!W_KN) {
             for (int idx = tid; idx < TBN * 8; idx += NTHREADS) {
                 const int r = idx >> 3, c = idx & 7;
                 if (k0 + c * 8 >= K)
-                    *reinterpret_cast<uint4*>(&s_b[stage][kc_off(r, c)]) = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(s_b(stage) + kc_off(r, c)) = make_uint4(0, 0, 0, 0);
             }
         } else {
             for (int idx = tid; idx < BK * TBN / 8; idx += NTHREADS) {
                 const int k = idx / (TBN / 8), c = idx % (TBN / 8);
                 if (k0 + k >= K)
-                    *reinterpret_cast<uint4*>(&s_b[stage][k * TBN + c * 8]) = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(s_b(stage) + k * TBN + c * 8) = make_uint4(0, 0, 0, 0);
             }
         }
     };
@@ -364,8 +405,8 @@ void grouped_gemm_kernel(const GemmParams p) {
     bf16x8 fa[2][FM], fb[2][FN];
     // fragments of half-stage h (K elements h*32 .. h*32+31): stage h/2, half h%2
     auto load_frags = [&](int h) {
-        const uint16_t* sa = s_a[(h >> 1) % NSTAGE];
-        const uint16_t* sb = s_b[(h >> 1) % NSTAGE];
+        const uint16_t* sa = s_a((h >> 1) % NSTAGE);
+        const uint16_t* sb = s_b((h >> 1) % NSTAGE);
         const int half = h & 1;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
@@ -411,8 +452,228 @@ void grouped_gemm_kernel(const GemmParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ss][j], fa[ss][i], acc[i][j], 0, 0, 0);
     };
 
-    for (int t = slot; t < total; t += G) {
-        setup_tile(t);
+    // ---- streaming flavor (small experts): weight streaming.  Workgroups take
+    // items round-robin.  Per 64-wide K stage the weight panel holds 256 rows
+    // (K-contiguous weights; for SwiGLU wave w's 32 rows are 16 gate rows then
+    // the matching 16 up rows) or 256 columns (transposed weights), and the
+    // token panel 64 rows (rows past the expert's end repeat its last row).
+    // A 3-stage ring runs continuously across the items, so the copies of the
+    // next item are in flight while the current one finishes.  Each wave
+    // computes 32 weight rows against one or two 32-row token blocks.
+    constexpr int SX_EL = SMALL_M * BK;
+    constexpr int S_NST = 3, SW_EL = 256 * BK, S_EL = SW_EL + SX_EL;
+    constexpr int SW_PW = SW_EL * 2 / 1024 / NWAVES;   // weight-panel copies per wave per stage
+    constexpr int LPS_S = SW_PW + 1;
+    static_assert(SX_EL * 2 == NWAVES * 1024, "one token-panel copy per wave");
+    static_assert(S_NST * S_EL <= NSTAGE * (A_STAGE + B_STAGE), "streaming stages fit in LDS");
+    struct SItem { int e, row0, rows, col0; };
+    auto stream_items = [&](int t0) -> int {
+        const int n_my = (n_stream - t0 + G - 1) / G;
+        const int nq = n_my * kiters;
+        const uint32_t s_lds0 = lds_addr(s_buf);
+        auto item_of = [&](int i) -> SItem {
+            const int t = t0 + i * G;
+            SItem it;
+            it.e = uni(find_expert(s_spre, E, t));
+            it.row0 = uni(s_off[it.e]);
+            it.rows = uni(s_off[it.e + 1]) - it.row0;
+            it.col0 = (t - uni(s_spre[it.e])) * S_COLS;
+            return it;
+        };
+        auto issue_s = [&](const SItem& it, int kt, int slot_i) {
+            const int k0 = kt * BK;
+            const uint32_t base = s_lds0 + slot_i * (S_EL * 2);
+            const uint16_t* wb = p.w + static_cast<int64_t>(it.e) * p.w_expert_stride;
+#pragma unroll
+            for (int i = 0; i < SW_PW; ++i) {
+                const int pos = (wave * SW_PW + i) * 64 + lane;
+                uint32_t voff;
+                if constexpr (!W_KN) {
+                    const int r = pos >> 3;
+                    const int c = (pos & 7) ^ kswz(r);
+                    int wrow;
+                    if constexpr (EPI == EPI_SWIGLU) {
+                        const int q = r & 31;
+                        wrow = min(it.col0 + (r >> 5) * 16 + (q & 15), N - 1) + (q >= 16 ? p.up_off : 0);
+                    } else {
+                        wrow = min(it.col0 + r, N - 1);
+                    }
+                    voff = static_cast<uint32_t>((wrow * p.ldw + min(k0 + c * 8, K - 8)) * 2);
+                } else {
+                    const int kr = pos >> 5;
+                    const int c = (pos & 31) ^ nswz(kr);
+                    voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + c * 8, N - 8)) * 2);
+                }
+                dma16(wb, voff, base + (wave * SW_PW + i) * 1024);
+            }
+            const int pos = wave * 64 + lane;
+            const int r = pos >> 3;
+            const int c = (pos & 7) ^ kswz(r);
+            const uint16_t* xb = p.act + static_cast<int64_t>(it.row0) * K;
+            const uint32_t xoff = static_cast<uint32_t>((min(r, it.rows - 1) * K + min(k0 + c * 8, K - 8)) * 2);
+            dma16(xb, xoff, base + SW_EL * 2 + wave * 1024);
+        };
+        f32x16 sacc[2];
+        auto szero = [&]() {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[b][v] = 0.f;
+        };
+        // K positions >= K (last stage only) are zeroed in the fragments, so
+        // whatever the copies left there never enters a sum.
+        auto s_mma = [&](int slot_i, int kt, int nblk) {
+            const uint16_t* sw = s_buf + slot_i * S_EL;
+            const uint16_t* sx = sw + SW_EL;
+            const bool last = k_tail && kt == kiters - 1;
+#pragma unroll
+            for (int j = 0; j < BK / 16; ++j) {
+                if (last && kt * BK + j * 16 >= K) break;
+                const int ch = 2 * j + (lane >> 5);
+                bf16x8 wf;
+                if constexpr (!W_KN) {
+                    wf = *reinterpret_cast<const bf16x8*>(sw + kc_off(wave * 32 + (lane & 31), ch));
+                } else {
+                    const int g = lane >> 4;
+                    const int kb = j * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
+                    const int n = wave * 32 + 16 * (g & 1) + 4 * (lane & 3);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + nc_off<256>(kb, n))));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + nc_off<256>(kb + 4, n))));
+                    wf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+                bf16x8 xf0 = *reinterpret_cast<const bf16x8*>(sx + kc_off(lane & 31, ch));
+                bf16x8 xf1 = xf0;
+                if (nblk > 1) xf1 = *reinterpret_cast<const bf16x8*>(sx + kc_off(32 + (lane & 31), ch));
+                if (last && kt * BK + j * 16 + 8 * (lane >> 5) >= K) {
+                    const bf16x8 z = {};
+                    wf = z;
+                    xf0 = z;
+                    xf1 = z;
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf0, sacc[0], 0, 0, 0);
+                if (nblk > 1) sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf1, sacc[1], 0, 0, 0);
+            }
+        };
+        // Lane holds token (lane & 31) of block b and, for register v, panel row
+        // 8*(v/4) + 4*(lane/32) + v%4 of the wave's 32 rows.
+        auto s_epilogue = [&](const SItem& it, int nblk) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                if (b >= nblk) break;
+                const int tok = b * 32 + (lane & 31);
+                const bool rv = tok < it.rows;
+                const int64_t grow = it.row0 + tok;
+                if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = it.col0 + wave * 32 + 8 * g + 4 * (lane >> 5);
+                        if (rv && col < N) {
+                            const uint2 v = make_uint2(pack2(sacc[b][4 * g], sacc[b][4 * g + 1]),
+                                                       pack2(sacc[b][4 * g + 2], sacc[b][4 * g + 3]));
+                            *reinterpret_cast<uint2*>(p.out0 + grow * N + col) = v;
+                        }
+                    }
+                } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const int f = it.col0 + wave * 16 + 8 * g + 4 * (lane >> 5);
+                        uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            gb[x] = f2bf(sacc[b][4 * g + x]);
+                            ub[x] = f2bf(sacc[b][4 * g + 8 + x]);
+                            const float gg = bf2f(gb[x]);
+                            const float uu = bf2f(ub[x]);
+                            ab[x] = f2bf(gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu);
+                        }
+                        if (rv && f < N) {
+                            *reinterpret_cast<uint2*>(p.out0 + grow * N + f) =
+                                make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                            if (p.out1) {
+                                uint16_t* h = p.out1 + grow * (2 * N) + f;
+                                *reinterpret_cast<uint2*>(h) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                                *reinterpret_cast<uint2*>(h + N) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int f = it.col0 + wave * 32 + 8 * g + 4 * (lane >> 5);
+                        if (rv && f < N) {
+                            const uint16_t* hp = p.aux + grow * (2 * N) + f;
+                            const uint2 hg = *reinterpret_cast<const uint2*>(hp);
+                            const uint2 hu = *reinterpret_cast<const uint2*>(hp + N);
+                            const uint32_t gw[2] = {hg.x, hg.y};
+                            const uint32_t uw[2] = {hu.x, hu.y};
+                            float dg[4], du[4];
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) {
+                                const float gg = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
+                                const float uu = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
+                                const float da = bf2f(f2bf(sacc[b][4 * g + x]));
+                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+                                dg[x] = da * uu * sgm * (1.0f + gg * (1.0f - sgm));
+                                du[x] = da * gg * sgm;
+                            }
+                            uint16_t* dh = p.out0 + grow * (2 * N) + f;
+                            *reinterpret_cast<uint2*>(dh) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+                            *reinterpret_cast<uint2*>(dh + N) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+                        }
+                    }
+                }
+            }
+        };
+
+        szero();
+        SItem it_d = item_of(0);   // copy cursor
+        int d_i = 0, d_kt = 0;
+        auto advance = [&]() {
+            if (++d_kt == kiters) {
+                d_kt = 0;
+                if (++d_i < n_my) it_d = item_of(d_i);
+            }
+        };
+#pragma unroll
+        for (int q = 0; q < S_NST - 1; ++q)
+            if (q < nq) {
+                issue_s(it_d, d_kt, q);
+                advance();
+            }
+        SItem it_c = item_of(0);   // compute cursor
+        for (int q = 0; q < nq; ++q) {
+            const int kt = q % kiters;
+            // stage q (and any epilogue stores issued before stage q+1) has
+            // landed; stage q+1 may stay in flight
+            if (q + 1 < nq) wait_vmcnt<LPS_S>();
+            else wait_vmcnt<0>();
+            block_barrier();
+            const int nblk = it_c.rows > 32 ? 2 : 1;
+            s_mma(q % S_NST, kt, nblk);
+            if (kt == kiters - 1) {
+                s_epilogue(it_c, nblk);
+                szero();
+                if (q + 1 < nq) it_c = item_of(q / kiters + 1);
+            }
+            // every wave has read stage q-1: refill its slot.  Issued after the
+            // epilogue stores, so the next wait covers them too.
+            if (q + S_NST - 1 < nq) {
+                issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
+                advance();
+            }
+        }
+        // the tile loop reuses the LDS
+        block_barrier();
+        return t0 + n_my * G;
+    };
+
+    // ---- streaming flavor first (work items [0, n_stream)), then the tiles
+    int t = slot;
+    if (t < n_stream) t = uni(stream_items(t));
+    for (; t < total; t += G) {
+        setup_tile(t - n_stream);
 #pragma unroll
         for (int s = 0; s < NSTAGE; ++s)
             if (s < kiters) issue(s);
@@ -481,7 +742,7 @@ void grouped_gemm_kernel(const GemmParams p) {
         // Results go through a per-wave LDS staging area (the stage slots are
         // free now: 16 KiB per wave) so that global traffic is 16 bytes per lane
         // over whole row segments.
-        uint16_t* stg = (wave < 4 ? &s_a[0][0] : &s_b[0][0]) + (wave & 3) * 8192 + opaque;
+        uint16_t* stg = (wave < 4 ? s_a(0) : s_b(0)) + (wave & 3) * 8192 + opaque;
         const int wrow0 = c_row0 + GRP * WROWS;    // first token row of this wave
         if constexpr (EPI == EPI_STORE) {
             // [128 rows][64 cols] bf16 (128-byte rows); 8-byte unit u of row r at u ^ ((r >> 1) & 15)

@@ -70,6 +70,9 @@ def test_validation_before_any_hip_call():
     assert L.gg_forward_fc2(16, 32, 8, 64, 4, 64, 12, 4096, None) == INV           # F % 8
     assert L.gg_forward_fc2(16, 32, -1, 64, 4, 64, 128, 4096, None) == INV         # M < 0
     assert L.gg_forward_fc2(16, 32, 1 << 31, 64, 4, 64, 128, 4096, None) == INV    # M too large
+    assert L.gg_forward_fc2(16, 32, 8, 64, 1, 1 << 22, 8, 4096, None) == INV        # H too large
+    assert L.gg_forward_fc2(16, 32, 8, 64, 1, 64, 1 << 21, 4096, None) == INV       # 2F too large
+    assert L.gg_forward_fc2(16, 32, 8, 64, 1, 1 << 15, 1 << 14, 4096, None) == INV  # W1_e >= 2 GiB
     # null pointers
     assert L.gg_forward_fc1_swiglu(None, 32, 8, 64, 4, 64, 128, None, 4096, None) == INV
     assert L.gg_forward_fc1_swiglu(16, 32, 8, 64, 4, 64, 128, None, None, None) == INV
