@@ -84,6 +84,8 @@ def test_tiny_workload():
     ([300, 1, 0, 2, 130], 1024, 256),
     # around the small-expert (weight-streaming) threshold of 64 rows, K tails
     ([31, 32, 63, 64, 65, 0, 1], 136, 200),
+    # the maximum expert count: mostly 0..5 rows, one large expert in the middle
+    ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 64, 64),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
