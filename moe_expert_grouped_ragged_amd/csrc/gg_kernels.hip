@@ -139,17 +139,29 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>(GG_AS3(const_cast<T*>(p)))));
 }
 
-// Experts with at most SMALL_M rows take the weight-streaming flavor: one work
-// item per block of output columns covering all of the expert's rows, so each
-// weight byte is read once per pass.  Larger experts are cut into 256-row tiles.
+// Rows that do not fill a 256-row tile, if there are at most SMALL_M of them
+// (every row of a small expert, or the tail of a large one), take the
+// weight-streaming flavor: one work item per block of output columns covering
+// all those rows, so each weight byte is read once for them.
 constexpr int SMALL_M = 64;
+
+// How an expert with m rows is split: full 256-row tiles, and the rows left
+// over.  A remainder of at most SMALL_M rows (all the rows of a small expert,
+// or the tail of a large one) is streamed; a larger remainder is one more,
+// partial tile.
+__device__ __forceinline__ int tile_rows_of(int m) {
+    const int tail = m % 256;
+    return (tail > 0 && tail <= SMALL_M) ? m - tail : m;     // rows covered by tiles
+}
+__device__ __forceinline__ int tiles_m_of(int m) { return (tile_rows_of(m) + 255) / 256; }
+__device__ __forceinline__ bool streams_rows(int m) { return m > 0 && tile_rows_of(m) < m; }
 
 // Per-expert work counts and their exclusive prefix sums in LDS, for both
 // flavors: s_pre counts 256x256 tiles of the large experts, s_spre counts
 // streaming items of the small ones.  Offsets are clamped into [0, M] so that
 // bad offsets cannot index out of bounds.
 template <int NT>
-__device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M, int bm,
+__device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M,
                                                int tiles_n, int items_n, int* s_off, int* s_pre, int* s_spre) {
     const int tid = threadIdx.x;
     for (int e = tid; e <= E; e += NT) {
@@ -163,14 +175,8 @@ __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offse
         const int per = (E + 63) / 64;
         const int e0 = lane * per;
         const int e1 = min(E, e0 + per);
-        auto big = [&](int e) {
-            const int m = max(0, s_off[e + 1] - s_off[e]);
-            return m > SMALL_M ? ((m + bm - 1) / bm) * tiles_n : 0;
-        };
-        auto small = [&](int e) {
-            const int m = max(0, s_off[e + 1] - s_off[e]);
-            return (m > 0 && m <= SMALL_M) ? items_n : 0;
-        };
+        auto big = [&](int e) { return tiles_m_of(max(0, s_off[e + 1] - s_off[e])) * tiles_n; };
+        auto small = [&](int e) { return streams_rows(max(0, s_off[e + 1] - s_off[e])) ? items_n : 0; };
         int sum = 0, ssum = 0;
         for (int e = e0; e < e1; ++e) {
             sum += big(e);
@@ -242,11 +248,12 @@ void grouped_gemm_kernel(const GemmParams p) {
     const int E = p.E, M = p.M, K = p.K, N = p.N;
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int tiles_n = (N + TILE_COLS - 1) / TILE_COLS;
-    // streaming flavor: an item is all rows of one small expert x S_COLS output
+    // streaming flavor: an item is the streamed rows of one expert x S_COLS output
     // columns (256 weight rows: for SwiGLU 128 gate rows and the matching 128 up rows)
     constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 128 : 256;
     const int items_n = (N + S_COLS - 1) / S_COLS;
-    build_schedule<NTHREADS>(p.offsets, E, M, TBM, tiles_n, items_n, s_off, s_pre, s_spre);
+    static_assert(TBM == 256, "tile_rows_of assumes 256-row tiles");
+    build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, s_off, s_pre, s_spre);
     const int n_stream = uni(s_spre[E]);
     const int total = n_stream + uni(s_pre[E]);
 
@@ -280,7 +287,7 @@ void grouped_gemm_kernel(const GemmParams p) {
         const int local = t - uni(s_pre[e]);
         const int rb = uni(s_off[e]);
         row_end = uni(s_off[e + 1]);
-        const int tiles_m = (row_end - rb + TBM - 1) / TBM;
+        const int tiles_m = tiles_m_of(row_end - rb);
         row0 = rb + (local % tiles_m) * TBM;
         col0 = (local / tiles_m) * TILE_COLS;
         a_base = p.act + static_cast<int64_t>(row0) * K;
@@ -475,8 +482,9 @@ void grouped_gemm_kernel(const GemmParams p) {
             const int t = t0 + i * G;
             SItem it;
             it.e = uni(find_expert(s_spre, E, t));
-            it.row0 = uni(s_off[it.e]);
-            it.rows = uni(s_off[it.e + 1]) - it.row0;
+            const int rb = uni(s_off[it.e]), re = uni(s_off[it.e + 1]);
+            it.row0 = rb + tile_rows_of(re - rb);   // the rows the tiles leave
+            it.rows = re - it.row0;
             it.col0 = (t - uni(s_spre[it.e])) * S_COLS;
             return it;
         };
