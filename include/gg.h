@@ -66,7 +66,7 @@ typedef enum {
     GG_OK = 0,
     GG_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, E/H/F/M out of range */
     GG_ERR_MISALIGNED = 2,         /* a tensor pointer is not 16-byte aligned */
-    GG_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
+    GG_ERR_UNSUPPORTED_DEVICE = 3, /* the stream's device (the current device for the null stream) is not gfx950 */
     GG_ERR_WORKSPACE_TOO_SMALL = 4,/* packed_bytes or workspace_bytes too small */
     GG_ERR_ALIASING = 5,           /* an output overlaps an input or another output */
     GG_ERR_HIP = 6                 /* a HIP runtime call failed */

@@ -29,9 +29,17 @@ constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
-int current_device_info(DeviceInfo* out) {
+// Properties of the device the work will run on: the stream's device, or the
+// current device for the null stream.
+int device_info(hipStream_t stream, DeviceInfo* out) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return GG_ERR_HIP;
+    if (stream == nullptr) {
+        if (hipGetDevice(&dev) != hipSuccess) return GG_ERR_HIP;
+    } else {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return GG_ERR_HIP;
+        dev = static_cast<int>(d);
+    }
     if (dev < 0 || dev >= kMaxDevices) return GG_ERR_UNSUPPORTED_DEVICE;
     std::lock_guard<std::mutex> lock(g_dev_mu);
     DeviceInfo& d = g_dev[dev];
@@ -166,7 +174,7 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, cons
         if (w2[e] != d2 && overlap(range_of(w2[e], w2_bytes), whole)) return GG_ERR_ALIASING;
     }
     DeviceInfo info;
-    const int st = current_device_info(&info);
+    const int st = device_info(stream, &info);
     if (st != GG_OK) return st;
     for (int64_t e = 0; e < E; ++e) {
         void* d1 = base + e * per_expert;
@@ -197,7 +205,7 @@ int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M, cons
     if (h1_out) outs.push_back(range_of(h1_out, M * 2 * F * 2));
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
     DeviceInfo info;
-    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = device_info(stream, &info)) != GG_OK) return st;
     if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
     gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
     p.act = static_cast<const uint16_t*>(x);
@@ -222,7 +230,7 @@ int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void*
     std::vector<Range> outs = {range_of(y, M * H * 2)};
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
     DeviceInfo info;
-    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = device_info(stream, &info)) != GG_OK) return st;
     if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
     gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
     p.w = static_cast<const uint16_t*>(packed) + 2 * F * H;
@@ -251,7 +259,7 @@ int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, 
                                range_of(dx, M * H * 2)};
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
     DeviceInfo info;
-    if ((st = current_device_info(&info)) != GG_OK) return st;
+    if ((st = device_info(stream, &info)) != GG_OK) return st;
     if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
     // dA = dY W2_e, then the SwiGLU derivative with the saved H1 -> dH1 (workspace)
     gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
@@ -279,7 +287,7 @@ int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream)
     if (!in || !out) return GG_ERR_INVALID_ARGUMENT;
     if (overlap(range_of(in, n * 4), range_of(out, n * 2))) return GG_ERR_ALIASING;
     DeviceInfo info;
-    const int st = current_device_info(&info);
+    const int st = device_info(stream, &info);
     if (st != GG_OK) return st;
     return gg::launch_round_bf16(in, out, n, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }

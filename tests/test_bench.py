@@ -1,0 +1,32 @@
+"""Host-side checks of the benchmark script (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+
+
+def test_cpu_baseline_on_the_tiny_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    import workload
+    case = workload.draw_case(workload.by_name("tiny_e4_h64_f128"))
+    rec = bench.cpu_baseline(case, 0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1 and rec["seconds"] > 0
+    assert "routed rows" in rec["sample"]
+
+
+def test_algorithmic_bytes_counts_only_experts_with_rows():
+    sys.path.insert(0, ROOT)
+    import bench
+    fwd, dg = bench.algorithmic_bytes(M=10, H=8, F=16, n_live=3)
+    assert fwd == 6 * 8 * 16 * 3 + 4 * 10 * 8 + 8 * 10 * 16
+    assert dg == 6 * 8 * 16 * 3 + 4 * 10 * 8 + 12 * 10 * 16
