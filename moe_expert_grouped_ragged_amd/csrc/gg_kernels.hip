@@ -250,7 +250,8 @@ void grouped_gemm_kernel(const GemmParams p) {
     const int tiles_n = (N + TILE_COLS - 1) / TILE_COLS;
     // streaming flavor: an item is the streamed rows of one expert x S_COLS output
     // columns (256 weight rows: for SwiGLU 128 gate rows and the matching 128 up rows)
-    constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 128 : 256;
+    constexpr int S_ROWS = 192;                                   // weight rows per item
+    constexpr int S_COLS = (EPI == EPI_SWIGLU) ? S_ROWS / 2 : S_ROWS;
     const int items_n = (N + S_COLS - 1) / S_COLS;
     static_assert(TBM == 256, "tile_rows_of assumes 256-row tiles");
     build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, s_off, s_pre, s_spre);
@@ -460,18 +461,23 @@ void grouped_gemm_kernel(const GemmParams p) {
     };
 
     // ---- streaming flavor (small experts): weight streaming.  Workgroups take
-    // items round-robin.  Per 64-wide K stage the weight panel holds 256 rows
+    // items round-robin.  Per 64-wide K stage the weight panel holds S_ROWS rows
     // (K-contiguous weights; for SwiGLU wave w's 32 rows are 16 gate rows then
-    // the matching 16 up rows) or 256 columns (transposed weights), and the
+    // the matching 16 up rows) or S_ROWS columns (transposed weights), and the
     // token panel 64 rows (rows past the expert's end repeat its last row).
-    // A 3-stage ring runs continuously across the items, so the copies of the
-    // next item are in flight while the current one finishes.  Each wave
-    // computes 32 weight rows against one or two 32-row token blocks.
+    // A 4-stage ring of 32 KiB runs continuously across the items, so the
+    // copies of the next item are in flight while the current one finishes.
+    // Waves w < S_WAVES compute 32 weight rows each against one or two 32-row
+    // token blocks; every wave copies.
     constexpr int SX_EL = SMALL_M * BK;
-    constexpr int S_NST = 3, SW_EL = 256 * BK, S_EL = SW_EL + SX_EL;
+    constexpr int S_NST = 4, SW_EL = S_ROWS * BK, S_EL = SW_EL + SX_EL;
     constexpr int SW_PW = SW_EL * 2 / 1024 / NWAVES;   // weight-panel copies per wave per stage
     constexpr int LPS_S = SW_PW + 1;
-    static_assert(SX_EL * 2 == NWAVES * 1024, "one token-panel copy per wave");
+    constexpr int S_WAVES = S_ROWS / 32;              // waves with weight rows to compute
+    constexpr int S_CPR = S_ROWS / 8;                 // 16-byte chunks per transposed-panel row
+    // transposed panels [64 k][S_ROWS n]: chunk c of row k at c ^ (2 * (k & 3)),
+    // which keeps every chunk inside its aligned group of 8
+    auto snc_off = [](int k, int n) { return k * S_ROWS + (((n >> 3) ^ ((k & 3) << 1)) << 3) + (n & 7); };
     static_assert(S_NST * S_EL <= NSTAGE * (A_STAGE + B_STAGE), "streaming stages fit in LDS");
     struct SItem { int e, row0, rows, col0; };
     auto stream_items = [&](int t0) -> int {
@@ -508,8 +514,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                     }
                     voff = static_cast<uint32_t>((wrow * p.ldw + min(k0 + c * 8, K - 8)) * 2);
                 } else {
-                    const int kr = pos >> 5;
-                    const int c = (pos & 31) ^ nswz(kr);
+                    const int kr = pos / S_CPR;
+                    const int c = (pos % S_CPR) ^ ((kr & 3) << 1);
                     voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + c * 8, N - 8)) * 2);
                 }
                 dma16(wb, voff, base + (wave * SW_PW + i) * 1024);
@@ -546,9 +552,9 @@ void grouped_gemm_kernel(const GemmParams p) {
                     const int kb = j * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
                     const int n = wave * 32 + 16 * (g & 1) + 4 * (lane & 3);
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + nc_off<256>(kb, n))));
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb, n))));
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + nc_off<256>(kb + 4, n))));
+                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb + 4, n))));
                     wf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
                 bf16x8 xf0 = *reinterpret_cast<const bf16x8*>(sx + kc_off(lane & 31, ch));
@@ -644,29 +650,31 @@ void grouped_gemm_kernel(const GemmParams p) {
                 if (++d_i < n_my) it_d = item_of(d_i);
             }
         };
-#pragma unroll
         for (int q = 0; q < S_NST - 1; ++q)
             if (q < nq) {
                 issue_s(it_d, d_kt, q);
                 advance();
             }
         SItem it_c = item_of(0);   // compute cursor
+        const bool s_mma_wave = wave < S_WAVES;
         for (int q = 0; q < nq; ++q) {
             const int kt = q % kiters;
-            // stage q (and any epilogue stores issued before stage q+1) has
-            // landed; stage q+1 may stay in flight
-            if (q + 1 < nq) wait_vmcnt<LPS_S>();
+            // stage q (and any epilogue stores issued before later stages) has
+            // landed; up to S_NST - 2 later stages may stay in flight
+            const int newer = min(S_NST - 2, nq - 1 - q);
+            if (newer >= 2) wait_vmcnt<2 * LPS_S>();
+            else if (newer == 1) wait_vmcnt<LPS_S>();
             else wait_vmcnt<0>();
             block_barrier();
             const int nblk = it_c.rows > 32 ? 2 : 1;
-            s_mma(q % S_NST, kt, nblk);
+            if (s_mma_wave) s_mma(q % S_NST, kt, nblk);
             if (kt == kiters - 1) {
-                s_epilogue(it_c, nblk);
+                if (s_mma_wave) s_epilogue(it_c, nblk);
                 szero();
                 if (q + 1 < nq) it_c = item_of(q / kiters + 1);
             }
             // every wave has read stage q-1: refill its slot.  Issued after the
-            // epilogue stores, so the next wait covers them too.
+            // epilogue stores, so the later waits cover them too.
             if (q + S_NST - 1 < nq) {
                 issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
                 advance();
