@@ -102,6 +102,16 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wait states between the last MFMA and the first read of its accumulators.
+// The compiler cannot count them where the read is inline assembly or where
+// a branch skipped the last MFMA, so the epilogues issue them explicitly
+// (24, more than a 16-pass MFMA needs).
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 template <typename T>
 __device__ __forceinline__ const T* uni_ptr(const T* ptr) {
     const uint64_t v = reinterpret_cast<uint64_t>(ptr);
@@ -573,6 +583,7 @@ void grouped_gemm_kernel(const GemmParams p) {
         // Lane holds token (lane & 31) of block b and, for register v, panel row
         // 8*(v/4) + 4*(lane/32) + v%4 of the wave's 32 rows.
         auto s_epilogue = [&](const SItem& it, int nblk) {
+            mfma_drain();
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 if (b >= nblk) break;
@@ -752,6 +763,7 @@ void grouped_gemm_kernel(const GemmParams p) {
         int opaque = 0;
         asm volatile("" : "+s"(opaque));
         const int c_row0 = row0 + opaque, c_row_end = row_end, c_col0 = col0 + opaque;
+        mfma_drain();
 
         // ---- epilogue.  Lane holds token row (lane & 31) of each token fragment
         // and, for register v, weight-panel row (v/4)*8 + (lane/32)*4 + v%4.

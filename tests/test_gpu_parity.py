@@ -82,6 +82,9 @@ def test_tiny_workload():
     ([513, 0, 0], 72, 264),
     ([0, 0, 40], 64, 8),
     ([300, 1, 0, 2, 130], 1024, 256),
+    # one K stage (H = 64) with one- and two-block streaming items: the
+    # accumulators are read right after the last MFMA
+    ([5, 0, 7, 33], 64, 64),
     # around the small-expert (weight-streaming) threshold of 64 rows, K tails
     ([31, 32, 63, 64, 65, 0, 1], 136, 200),
     # the maximum expert count: mostly 0..5 rows, one large expert in the middle
