@@ -105,6 +105,81 @@ def cpu_baseline(case, target_s: float):
             "rows_per_s": n / t, "seconds": t}
 
 
+def launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args):
+    """Step time (forward + dgrad) on the same data: one persistent launch per
+    GEMM (the library as shipped) against one launch per expert and GEMM (E = 1
+    calls on each expert's rows and packed weights, the split known on the
+    host), each issued from Python and as a HIP-graph replay (the replay
+    removes the host launch cost and leaves the kernels' own)."""
+    import numpy as np
+    import torch
+    E, H, F = case.E, case.H, case.F
+    off_h = case.offsets
+    per = 3 * F * H
+    live = [e for e in range(E) if off_h[e + 1] > off_h[e]]
+    one = {e: torch.tensor([0, int(off_h[e + 1] - off_h[e])], dtype=torch.int64, device=x.device) for e in live}
+
+    def grouped():
+        gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
+        gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
+        gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
+
+    def per_expert():
+        for e in live:
+            s0, s1 = int(off_h[e]), int(off_h[e + 1])
+            pk = packed[e * per:(e + 1) * per]
+            gg.gg_forward_fc1_swiglu(x[s0:s1], one[e], pk, 1, H, F, h1_out=h1[s0:s1], a_out=a[s0:s1])
+            gg.gg_forward_fc2(a[s0:s1], one[e], pk, 1, H, F, y=y[s0:s1])
+            gg.gg_dgrad(dy[s0:s1], h1[s0:s1], one[e], pk, 1, H, F, workspace=ws[s0:s1], dx=dx[s0:s1])
+
+    def timed(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    ms_grouped = timed(grouped, args.steps)
+    ms_per_expert = timed(per_expert, args.steps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        grouped()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grouped()
+    ms_graph = timed(graph.replay, args.steps)
+    # the per-expert loop captured as well: no host launch cost left, only the
+    # per-expert kernels themselves
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        per_expert()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_pe = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_pe):
+        per_expert()
+    ms_graph_pe = timed(graph_pe.replay, args.steps)
+    M = case.M
+    return {"launch_ab": {"workload": args.workload, "experts_with_rows": len(live),
+                          "launches_per_step": {"grouped": 4, "per_expert": 4 * len(live)},
+                          "ms_per_step": {"grouped": ms_grouped, "per_expert": ms_per_expert,
+                                          "grouped_graph_replay": ms_graph,
+                                          "per_expert_graph_replay": ms_graph_pe},
+                          "tokens_per_s": {"grouped": case.T / (ms_grouped * 1e-3),
+                                           "per_expert": case.T / (ms_per_expert * 1e-3),
+                                           "grouped_graph_replay": case.T / (ms_graph * 1e-3),
+                                           "per_expert_graph_replay": case.T / (ms_graph_pe * 1e-3)},
+                          "speedup_grouped_vs_per_expert": ms_per_expert / ms_grouped,
+                          "speedup_grouped_vs_per_expert_both_replayed": ms_graph_pe / ms_graph,
+                          "routed_rows": M, "steps": args.steps, "warmup": args.warmup}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +188,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch-ab", action="store_true",
+                    help="instead of the benchmark line, compare one grouped launch per GEMM with one "
+                         "launch per expert (the same library, E=1 calls) and with a HIP-graph replay "
+                         "of the grouped step; prints one JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -177,6 +256,10 @@ def main():
             ev["fc1"].append((e0, e1))
             ev["fc2"].append((e1, e2))
             ev["dgrad"].append((e2, e3))
+
+    if args.launch_ab:
+        print(json.dumps(launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args)), flush=True)
+        return
 
     for _ in range(args.warmup):
         step(False)
