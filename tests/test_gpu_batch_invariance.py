@@ -1,0 +1,85 @@
+"""Batch invariance: a token row's results do not depend on the rest of the batch.
+
+One set of token rows routed to one expert's weights is computed inside many
+different batches: alone (a small expert, weight-streaming flavor), as the
+head of a large expert (256-row tiles), as the streamed tail of a large
+expert, shifted by row counts that are not multiples of 32 (so the rows land
+in other MFMA lanes), in another expert slot, and beside other experts.  Both
+flavors accumulate the same MFMA k-steps in the same order into fp32
+accumulators that start at zero, and share the epilogue arithmetic, so H1, A,
+Y, dH1 and dX of those rows must be bitwise equal in every batch."""
+import numpy as np
+import pytest
+import torch
+
+import workload
+from gpu_harness import DeviceCase, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _layouts(R):
+    """name -> per-slot list of segments; a segment is ("R", n) for the rows
+    under test or ("o", n) for other rows.  The rows under test always use the
+    test weights; every slot not holding them uses the other weights."""
+    return {
+        "alone": [[("R", R)]],
+        "head_of_large": [[("R", R), ("o", 300)]],
+        "streamed_tail": [[("o", 256), ("R", R)]],
+        "shifted_in_small": [[("o", 7), ("R", R)]],
+        "shifted_in_tile": [[("o", 13), ("R", R), ("o", 300)]],
+        "shifted_tail": [[("o", 259), ("R", R)]],
+        "other_slot": [[("o", 100)], [], [("o", 3), ("R", R)], [("o", 70)]],
+        "beside_others": [[("R", R)], [("o", 300)], [("o", 256)], [("o", 70)]],
+    }
+
+
+def _run(layout, R, base):
+    xs, dys, counts, w1s, w2s = [], [], [], [], []
+    other = 0
+    where = None
+    for slot in layout:
+        n_slot = 0
+        has_r = any(kind == "R" for kind, _ in slot)
+        for kind, n in slot:
+            if kind == "R":
+                where = sum(counts) + n_slot
+                xs.append(base.x[:R]); dys.append(base.dy[:R])
+            else:
+                xs.append(base.x[R + other:R + other + n]); dys.append(base.dy[R + other:R + other + n])
+                other += n
+            n_slot += n
+        counts.append(n_slot)
+        w1s.append(base.w1[0 if has_r else 1]); w2s.append(base.w2[0 if has_r else 1])
+    counts = np.asarray(counts, dtype=np.int64)
+    off = workload.offsets_from_counts(counts)
+    x = torch.cat(xs) if xs else base.x[:0]
+    dy = torch.cat(dys) if dys else base.dy[:0]
+    assert x.shape[0] == off[-1] and other <= base.x.shape[0] - R
+    case = workload.Case("invariance", len(counts), base.H, base.F, int(counts.sum()), counts, off,
+                         torch.stack(w1s), torch.stack(w2s), x, dy)
+    dc = DeviceCase(case)
+    h1, a, y = dc.forward()
+    dh1, dx = dc.dgrad(h1)
+    torch.cuda.synchronize()
+    sl = slice(where, where + R)
+    return {"h1": h1[sl].cpu(), "a": a[sl].cpu(), "y": y[sl].cpu(), "dh1": dh1[sl].cpu(),
+            "dx": dx[sl].cpu()}
+
+
+@pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64)])
+def test_rows_are_batch_invariant(H, F, R):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    base = workload.custom_case([R, 700], H, F, seed=31)
+    ref = None
+    for name, layout in _layouts(R).items():
+        log(f"[invariance] H={H} F={F} R={R} {name}")
+        got = _run(layout, R, base)
+        if ref is None:
+            ref = got
+            continue
+        for k in ref:
+            same = got[k].view(torch.int16) == ref[k].view(torch.int16)
+            assert bool(same.all()), (name, k, int((~same).sum()))
+    log(f"[invariance] H={H} F={F} R={R}: every layout bitwise equal to 'alone'")
