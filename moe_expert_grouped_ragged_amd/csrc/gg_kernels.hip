@@ -478,12 +478,18 @@ void grouped_gemm_kernel(const GemmParams p) {
     // A 4-stage ring of 32 KiB runs continuously across the items, so the
     // copies of the next item are in flight while the current one finishes.
     // Waves w < S_WAVES compute 32 weight rows each against one or two 32-row
-    // token blocks; every wave copies.
+    // token blocks and store the results; the other two waves issue every
+    // copy, so a copy wave's vmcnt counts copies only (vmcnt retires in
+    // order: a store queued among the copies would be waited for with them).
     constexpr int SX_EL = SMALL_M * BK;
     constexpr int S_NST = 4, SW_EL = S_ROWS * BK, S_EL = SW_EL + SX_EL;
-    constexpr int SW_PW = SW_EL * 2 / 1024 / NWAVES;   // weight-panel copies per wave per stage
-    constexpr int LPS_S = SW_PW + 1;
     constexpr int S_WAVES = S_ROWS / 32;              // waves with weight rows to compute
+    constexpr int S_CWAVES = NWAVES - S_WAVES;        // copy waves
+    constexpr int SW_PW = SW_EL * 2 / 1024 / S_CWAVES; // weight-panel copies per copy wave per stage
+    constexpr int SX_PW = SX_EL * 2 / 1024 / S_CWAVES; // token-panel copies per copy wave per stage
+    constexpr int LPS_S = SW_PW + SX_PW;
+    static_assert(SW_PW * S_CWAVES * 1024 == SW_EL * 2 && SX_PW * S_CWAVES * 1024 == SX_EL * 2, "copy split");
+    static_assert(3 * LPS_S < 64, "vmcnt range");
     constexpr int S_CPR = S_ROWS / 8;                 // 16-byte chunks per transposed-panel row
     // transposed panels [64 k][S_ROWS n]: chunk c of row k at c ^ (2 * (k & 3)),
     // which keeps every chunk inside its aligned group of 8
@@ -505,12 +511,14 @@ void grouped_gemm_kernel(const GemmParams p) {
             return it;
         };
         auto issue_s = [&](const SItem& it, int kt, int slot_i) {
+            if (wave < S_WAVES) return;
+            const int cw = wave - S_WAVES;
             const int k0 = kt * BK;
             const uint32_t base = s_lds0 + slot_i * (S_EL * 2);
             const uint16_t* wb = p.w + static_cast<int64_t>(it.e) * p.w_expert_stride;
 #pragma unroll
             for (int i = 0; i < SW_PW; ++i) {
-                const int pos = (wave * SW_PW + i) * 64 + lane;
+                const int pos = (cw * SW_PW + i) * 64 + lane;
                 uint32_t voff;
                 if constexpr (!W_KN) {
                     const int r = pos >> 3;
@@ -528,14 +536,17 @@ void grouped_gemm_kernel(const GemmParams p) {
                     const int c = (pos % S_CPR) ^ ((kr & 3) << 1);
                     voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + c * 8, N - 8)) * 2);
                 }
-                dma16(wb, voff, base + (wave * SW_PW + i) * 1024);
+                dma16(wb, voff, base + (cw * SW_PW + i) * 1024);
             }
-            const int pos = wave * 64 + lane;
-            const int r = pos >> 3;
-            const int c = (pos & 7) ^ kswz(r);
             const uint16_t* xb = p.act + static_cast<int64_t>(it.row0) * K;
-            const uint32_t xoff = static_cast<uint32_t>((min(r, it.rows - 1) * K + min(k0 + c * 8, K - 8)) * 2);
-            dma16(xb, xoff, base + SW_EL * 2 + wave * 1024);
+#pragma unroll
+            for (int i = 0; i < SX_PW; ++i) {
+                const int pos = (cw * SX_PW + i) * 64 + lane;
+                const int r = pos >> 3;
+                const int c = (pos & 7) ^ kswz(r);
+                const uint32_t xoff = static_cast<uint32_t>((min(r, it.rows - 1) * K + min(k0 + c * 8, K - 8)) * 2);
+                dma16(xb, xoff, base + SW_EL * 2 + (cw * SX_PW + i) * 1024);
+            }
         };
         f32x16 sacc[2];
         auto szero = [&]() {
@@ -670,12 +681,14 @@ void grouped_gemm_kernel(const GemmParams p) {
         const bool s_mma_wave = wave < S_WAVES;
         for (int q = 0; q < nq; ++q) {
             const int kt = q % kiters;
-            // stage q (and any epilogue stores issued before later stages) has
-            // landed; up to S_NST - 2 later stages may stay in flight
+            // the copy waves wait for stage q (up to S_NST - 2 later stages stay
+            // in flight); the barrier publishes it to the compute waves
             const int newer = min(S_NST - 2, nq - 1 - q);
-            if (newer >= 2) wait_vmcnt<2 * LPS_S>();
-            else if (newer == 1) wait_vmcnt<LPS_S>();
-            else wait_vmcnt<0>();
+            if (!s_mma_wave) {
+                if (newer >= 2) wait_vmcnt<2 * LPS_S>();
+                else if (newer == 1) wait_vmcnt<LPS_S>();
+                else wait_vmcnt<0>();
+            }
             block_barrier();
             const int nblk = it_c.rows > 32 ? 2 : 1;
             if (s_mma_wave) s_mma(q % S_NST, kt, nblk);
@@ -684,8 +697,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                 szero();
                 if (q + 1 < nq) it_c = item_of(q / kiters + 1);
             }
-            // every wave has read stage q-1: refill its slot.  Issued after the
-            // epilogue stores, so the later waits cover them too.
+            // every wave has read stage q-1 (the barrier above waited for the
+            // reads): the copy waves refill its slot
             if (q + S_NST - 1 < nq) {
                 issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
                 advance();
