@@ -58,9 +58,16 @@ def _load():
             lib.oracle_swiglu_f32.argtypes = [i64, i64, p, p, p]
             lib.oracle_fc2_f32.argtypes = [i64, i64, i64, p, p, p, p]
             lib.oracle_dgrad_fc1_f32.argtypes = [i64, i64, i64, p, p, p, p]
+            i32 = ctypes.c_int
+            lib.oracle_glu_f32.argtypes = [i64, i64, p, i32, p, p, p]
+            for name in ("oracle_forward_glu_f32", "oracle_forward_glu_f64"):
+                getattr(lib, name).argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, p, p]
+            for name in ("oracle_dgrad_glu_f32", "oracle_dgrad_glu_f64"):
+                getattr(lib, name).argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, p, p, p]
             for name in ("oracle_round_bf16", "oracle_forward_f32", "oracle_forward_f64",
                          "oracle_dgrad_f32", "oracle_dgrad_f64", "oracle_swiglu_f32", "oracle_fc2_f32",
-                         "oracle_dgrad_fc1_f32"):
+                         "oracle_dgrad_fc1_f32", "oracle_glu_f32", "oracle_forward_glu_f32",
+                         "oracle_forward_glu_f64", "oracle_dgrad_glu_f32", "oracle_dgrad_glu_f64"):
                 getattr(lib, name).restype = None
             _lib = lib
     return _lib
@@ -217,6 +224,113 @@ def dgrad64(dy, h1, offsets, w1, w2):
     _load().oracle_dgrad_f64(E, H, F, _ptr(off), _ptr(dy), _ptr(h1), _ptr(w1), _ptr(w2),
                              _ptr(dh1), _ptr(dx))
     return {"dh1": dh1, "dx": dx}
+
+
+ACTIVATIONS = {"swiglu": 0, "qgeglu": 1}
+
+
+def _act(act) -> int:
+    if isinstance(act, str):
+        return ACTIVATIONS[act]
+    if int(act) not in ACTIVATIONS.values():
+        raise ValueError(f"unknown activation {act}")
+    return int(act)
+
+
+def _probs(probs, M: int, dtype=np.float32):
+    """Optional per-row probabilities [M] -> contiguous array (or None)."""
+    if probs is None:
+        return None
+    if hasattr(probs, "detach"):
+        probs = probs.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(probs, dtype=dtype))
+    if a.shape != (M,):
+        raise ValueError("probs must be [M]")
+    return a
+
+
+def _optr(a):
+    return None if a is None else a.ctypes.data
+
+
+def glu(h1, offsets, act="swiglu", probs=None):
+    """Activation alone from a given H1 [M,2F]: a [M,F] = bf16(p * act(gate) * up)."""
+    h132 = _as_f32(h1)
+    M, twoF = h132.shape
+    F = twoF // 2
+    off = _check_offsets(offsets, np.asarray(offsets).shape[0] - 1, M)
+    pr = _probs(probs, M)
+    a = np.full((M, F), np.nan, np.float32)
+    _load().oracle_glu_f32(off.shape[0] - 1, F, _ptr(off), _act(act), _optr(pr), _ptr(h132), _ptr(a))
+    return a
+
+
+def forward_glu(x, offsets, w1, w2, act="swiglu", probs=None):
+    """forward() with the activation chosen by act ("swiglu" | "qgeglu") and
+    optional fp32 per-row router probabilities probs [M] weighting it."""
+    x32, w132, w232 = _as_f32(x), _as_f32(w1), _as_f32(w2)
+    E, twoF, H = w132.shape
+    F = twoF // 2
+    M = x32.shape[0]
+    assert w232.shape == (E, H, F) and x32.shape == (M, H)
+    off = _check_offsets(offsets, E, M)
+    pr = _probs(probs, M)
+    h1 = np.full((M, 2 * F), np.nan, np.float32)
+    a = np.full((M, F), np.nan, np.float32)
+    y = np.full((M, H), np.nan, np.float32)
+    _load().oracle_forward_glu_f32(E, H, F, _ptr(off), _act(act), _optr(pr), _ptr(x32), _ptr(w132),
+                                   _ptr(w232), _ptr(h1), _ptr(a), _ptr(y))
+    return {"h1": h1, "a": a, "y": y}
+
+
+def dgrad_glu(dy, h1, offsets, w1, w2, act="swiglu", probs=None):
+    """dgrad() for forward_glu: returns dh1, dx and dprobs [M] (fp32, NaN
+    outside the routed rows)."""
+    dy32, h132, w132, w232 = _as_f32(dy), _as_f32(h1), _as_f32(w1), _as_f32(w2)
+    E, twoF, H = w132.shape
+    F = twoF // 2
+    M = dy32.shape[0]
+    assert h132.shape == (M, 2 * F) and w232.shape == (E, H, F)
+    off = _check_offsets(offsets, E, M)
+    pr = _probs(probs, M)
+    dh1 = np.full((M, 2 * F), np.nan, np.float32)
+    dx = np.full((M, H), np.nan, np.float32)
+    dp = np.full(M, np.nan, np.float32)
+    _load().oracle_dgrad_glu_f32(E, H, F, _ptr(off), _act(act), _optr(pr), _ptr(dy32), _ptr(h132),
+                                 _ptr(w132), _ptr(w232), _ptr(dh1), _ptr(dx), _ptr(dp))
+    return {"dh1": dh1, "dx": dx, "dprobs": dp}
+
+
+def forward_glu64(x, offsets, w1, w2, act="swiglu", probs=None):
+    """fp64 forward_glu without rounding."""
+    x, w1, w2 = (np.ascontiguousarray(v, dtype=np.float64) for v in (x, w1, w2))
+    E, twoF, H = w1.shape
+    F = twoF // 2
+    M = x.shape[0]
+    off = _check_offsets(offsets, E, M)
+    pr = _probs(probs, M, np.float64)
+    h1 = np.full((M, 2 * F), np.nan)
+    a = np.full((M, F), np.nan)
+    y = np.full((M, H), np.nan)
+    _load().oracle_forward_glu_f64(E, H, F, _ptr(off), _act(act), _optr(pr), _ptr(x), _ptr(w1), _ptr(w2),
+                                   _ptr(h1), _ptr(a), _ptr(y))
+    return {"h1": h1, "a": a, "y": y}
+
+
+def dgrad_glu64(dy, h1, offsets, w1, w2, act="swiglu", probs=None):
+    """fp64 dgrad_glu without rounding."""
+    dy, h1, w1, w2 = (np.ascontiguousarray(v, dtype=np.float64) for v in (dy, h1, w1, w2))
+    E, twoF, H = w1.shape
+    F = twoF // 2
+    M = dy.shape[0]
+    off = _check_offsets(offsets, E, M)
+    pr = _probs(probs, M, np.float64)
+    dh1 = np.full((M, 2 * F), np.nan)
+    dx = np.full((M, H), np.nan)
+    dp = np.full(M, np.nan)
+    _load().oracle_dgrad_glu_f64(E, H, F, _ptr(off), _act(act), _optr(pr), _ptr(dy), _ptr(h1), _ptr(w1),
+                                 _ptr(w2), _ptr(dh1), _ptr(dx), _ptr(dp))
+    return {"dh1": dh1, "dx": dx, "dprobs": dp}
 
 
 def sample_rows(offsets, rows):

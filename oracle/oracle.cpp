@@ -20,6 +20,19 @@
 // change"), so the oracle is that definition written out, one expert and one
 // row at a time.
 //
+// Weighted and QuickGeGLU variants (paged-stash pull request, "What does this
+// PR do" and "Validation": the fused activation is SwiGLU or QuickGeGLU, and
+// its weighted form takes the router probability of each routed row at the
+// activation boundary).  The pages name these activations but print no
+// formula; the reading used here is
+//     act(g) = g * sigmoid(c g),  c = 1 (SwiGLU) or 1.702 (QuickGeGLU)
+//     A      = p_r * act(gate) * up                 (p_r omitted: p_r = 1)
+//     dA     = dY W2_e
+//     dH1    = [p_r dA up act'(gate) | p_r dA act(gate)]
+//     dp_r   = sum_j dA[r, j] act(gate[r, j]) up[r, j]
+// with act'(g) = s (1 + c g (1 - s)), s = sigmoid(c g).  dp is an fp32 sum
+// over j in increasing order and is not rounded to bf16.
+//
 // Precision.  Two instantiations of the same code:
 //   float  : inputs are bf16 values held in fp32, every sum accumulates in
 //            fp32 in increasing index order, and H1, A, Y, dA, dH1, dX are
@@ -64,24 +77,36 @@ template <> float rnd<float>(float v) { return round_to_bf16(v); }
 template <> double rnd<double>(double v) { return v; }
 
 template <typename T> T sigmoid(T g) { return T(1) / (T(1) + std::exp(-g)); }
-template <typename T> T silu(T g) { return g / (T(1) + std::exp(-g)); }
 
-// SwiGLU for one routed row r: A[r, j] = silu(gate) * up with gate = H1[r, j],
-// up = H1[r, F + j] (the rounded H1 values).
+// Gated activations: 0 = SwiGLU, 1 = QuickGeGLU.
+enum { ACT_SWIGLU = 0, ACT_QGEGLU = 1 };
+
+// Slope c inside the sigmoid of the gate activation.
+template <typename T> T act_slope(int act) { return act == ACT_QGEGLU ? T(1.702) : T(1); }
+
+// act(g) = g * sigmoid(c g), written as g / (1 + exp(-c g)).  For SwiGLU c g is
+// g itself (c = 1 is exact).
+template <typename T> T gate_act(int act, T g) { return g / (T(1) + std::exp(-(act_slope<T>(act) * g))); }
+
+// Activation for one routed row r: A[r, j] = p_r * act(gate) * up with
+// gate = H1[r, j], up = H1[r, F + j] (the rounded H1 values); without probs
+// the product is act(gate) * up alone.
 template <typename T>
-void swiglu_row(int64_t r, int64_t F, const T* h1, T* a) {
+void glu_row(int64_t r, int64_t F, int act, const T* probs, const T* h1, T* a) {
     const T* h1r = h1 + r * 2 * F;
     T* ar = a + r * F;
     for (int64_t j = 0; j < F; ++j) {
         const T g = h1r[j];
         const T u = h1r[F + j];
-        ar[j] = rnd<T>(silu<T>(g) * u);
+        const T v = gate_act<T>(act, g) * u;
+        ar[j] = rnd<T>(probs ? probs[r] * v : v);
     }
 }
 
-// FC1 + SwiGLU for one routed row r of expert e: H1 row and A row.
+// FC1 + activation for one routed row r of expert e: H1 row and A row.
 template <typename T>
-void fc1_swiglu_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, T* h1, T* a) {
+void fc1_glu_row(int64_t r, int64_t H, int64_t F, int act, const T* probs, const T* x, const T* w1e,
+                 T* h1, T* a) {
     const T* xr = x + r * H;
     T* h1r = h1 + r * 2 * F;
     // FC1: H1[r, j] = sum_k X[r, k] * W1_e[j, k]
@@ -91,7 +116,7 @@ void fc1_swiglu_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, T
         for (int64_t k = 0; k < H; ++k) acc += xr[k] * wj[k];
         h1r[j] = rnd<T>(acc);
     }
-    swiglu_row<T>(r, F, h1, a);
+    glu_row<T>(r, F, act, probs, h1, a);
 }
 
 // FC2 for one routed row r of expert e: Y[r, n] = sum_j A[r, j] * W2_e[n, j].
@@ -109,17 +134,17 @@ void fc2_row(int64_t r, int64_t H, int64_t F, const T* a, const T* w2e, T* y) {
 
 // Forward for one routed row r of expert e.
 template <typename T>
-void forward_row(int64_t r, int64_t H, int64_t F, const T* x, const T* w1e, const T* w2e,
-                 T* h1, T* a, T* y) {
-    fc1_swiglu_row<T>(r, H, F, x, w1e, h1, a);
+void forward_row(int64_t r, int64_t H, int64_t F, int act, const T* probs, const T* x, const T* w1e,
+                 const T* w2e, T* h1, T* a, T* y) {
+    fc1_glu_row<T>(r, H, F, act, probs, x, w1e, h1, a);
     fc2_row<T>(r, H, F, a, w2e, y);
 }
 
-// dA and the SwiGLU derivative for one routed row r of expert e -> dH1 row.
-// acc is scratch of F elements.
+// dA and the activation derivative for one routed row r of expert e -> dH1
+// row (and dp_r when dprobs is given).  acc is scratch of F elements.
 template <typename T>
-void dswiglu_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const T* w2e, T* dh1,
-                 T* acc) {
+void dglu_row(int64_t r, int64_t H, int64_t F, int act, const T* probs, const T* dy, const T* h1,
+              const T* w2e, T* dh1, T* dprobs, T* acc) {
     const T* dyr = dy + r * H;
     const T* h1r = h1 + r * 2 * F;
     T* dh1r = dh1 + r * 2 * F;
@@ -131,16 +156,21 @@ void dswiglu_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, cons
         const T* wn = w2e + n * F;
         for (int64_t j = 0; j < F; ++j) acc[j] += d * wn[j];
     }
-    // dSwiGLU: d gate = dA * up * s * (1 + g (1 - s)), d up = dA * g * s,
-    // with s = sigmoid(g), g and up the saved (rounded) H1 values.
+    // d gate = p dA * up * s * (1 + c g (1 - s)), d up = p dA * g * s, with
+    // s = sigmoid(c g), g and up the saved (rounded) H1 values and dA rounded.
+    const T c = act_slope<T>(act);
+    T dp = 0;
     for (int64_t j = 0; j < F; ++j) {
         const T da = rnd<T>(acc[j]);
         const T g = h1r[j];
         const T u = h1r[F + j];
-        const T s = sigmoid<T>(g);
-        dh1r[j] = rnd<T>(da * u * s * (T(1) + g * (T(1) - s)));
-        dh1r[F + j] = rnd<T>(da * g * s);
+        const T s = sigmoid<T>(c * g);
+        const T dap = probs ? probs[r] * da : da;
+        dh1r[j] = rnd<T>(dap * u * s * (T(1) + c * g * (T(1) - s)));
+        dh1r[F + j] = rnd<T>(dap * g * s);
+        if (dprobs) dp += da * (gate_act<T>(act, g) * u);
     }
+    if (dprobs) dprobs[r] = dp;
 }
 
 // dX for one routed row r of expert e: dX[r, k] = sum_j dH1[r, j] * W1_e[j, k],
@@ -161,26 +191,27 @@ void dgrad_fc1_row(int64_t r, int64_t H, int64_t F, const T* dh1, const T* w1e, 
 // Input gradient for one routed row r of expert e.  acc is scratch of
 // max(F, H) elements.
 template <typename T>
-void dgrad_row(int64_t r, int64_t H, int64_t F, const T* dy, const T* h1, const T* w1e,
-               const T* w2e, T* dh1, T* dx, T* acc) {
-    dswiglu_row<T>(r, H, F, dy, h1, w2e, dh1, acc);
+void dgrad_row(int64_t r, int64_t H, int64_t F, int act, const T* probs, const T* dy, const T* h1,
+               const T* w1e, const T* w2e, T* dh1, T* dx, T* dprobs, T* acc) {
+    dglu_row<T>(r, H, F, act, probs, dy, h1, w2e, dh1, dprobs, acc);
     dgrad_fc1_row<T>(r, H, F, dh1, w1e, dx, acc);
 }
 
 template <typename T>
-void forward_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* x,
-                 const T* w1, const T* w2, T* h1, T* a, T* y) {
+void forward_all(int64_t E, int64_t H, int64_t F, const int64_t* off, int act, const T* probs,
+                 const T* x, const T* w1, const T* w2, T* h1, T* a, T* y) {
     for (int64_t e = 0; e < E; ++e) {
         const T* w1e = w1 + e * 2 * F * H;
         const T* w2e = w2 + e * H * F;
 #pragma omp parallel for schedule(static)
-        for (int64_t r = off[e]; r < off[e + 1]; ++r) forward_row<T>(r, H, F, x, w1e, w2e, h1, a, y);
+        for (int64_t r = off[e]; r < off[e + 1]; ++r)
+            forward_row<T>(r, H, F, act, probs, x, w1e, w2e, h1, a, y);
     }
 }
 
 template <typename T>
-void dgrad_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* dy, const T* h1,
-               const T* w1, const T* w2, T* dh1, T* dx) {
+void dgrad_all(int64_t E, int64_t H, int64_t F, const int64_t* off, int act, const T* probs,
+               const T* dy, const T* h1, const T* w1, const T* w2, T* dh1, T* dx, T* dprobs) {
     const int64_t n_acc = H > F ? H : F;
     for (int64_t e = 0; e < E; ++e) {
         const T* w1e = w1 + e * 2 * F * H;
@@ -190,7 +221,7 @@ void dgrad_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T* dy,
             std::vector<T> acc(n_acc);
 #pragma omp for schedule(static)
             for (int64_t r = off[e]; r < off[e + 1]; ++r)
-                dgrad_row<T>(r, H, F, dy, h1, w1e, w2e, dh1, dx, acc.data());
+                dgrad_row<T>(r, H, F, act, probs, dy, h1, w1e, w2e, dh1, dx, dprobs, acc.data());
         }
     }
 }
@@ -225,7 +256,15 @@ extern "C" {
 // SwiGLU alone, from a given H1 [M][2F] -> a [M][F], rows [offsets[0], offsets[E]).
 void oracle_swiglu_f32(int64_t E, int64_t F, const int64_t* offsets, const float* h1, float* a) {
 #pragma omp parallel for schedule(static)
-    for (int64_t r = offsets[0]; r < offsets[E]; ++r) swiglu_row<float>(r, F, h1, a);
+    for (int64_t r = offsets[0]; r < offsets[E]; ++r) glu_row<float>(r, F, ACT_SWIGLU, nullptr, h1, a);
+}
+
+// Weighted / QuickGeGLU activation alone, from a given H1: act 0 = SwiGLU,
+// 1 = QuickGeGLU; probs [M] fp32 or null.
+void oracle_glu_f32(int64_t E, int64_t F, const int64_t* offsets, int act, const float* probs,
+                    const float* h1, float* a) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = offsets[0]; r < offsets[E]; ++r) glu_row<float>(r, F, act, probs, h1, a);
 }
 
 // FC2 alone (the second step of the forward), from a given A [M][F] -> y [M][H].
@@ -252,7 +291,7 @@ void oracle_round_bf16(const float* in, float* out, int64_t n) {
 void oracle_forward_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
                         const float* x, const float* w1, const float* w2,
                         float* h1, float* a, float* y) {
-    forward_all<float>(E, H, F, offsets, x, w1, w2, h1, a, y);
+    forward_all<float>(E, H, F, offsets, ACT_SWIGLU, nullptr, x, w1, w2, h1, a, y);
 }
 
 // Input gradient, fp32 accumulation with bf16 rounding points.
@@ -260,20 +299,47 @@ void oracle_forward_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
 void oracle_dgrad_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
                       const float* dy, const float* h1, const float* w1, const float* w2,
                       float* dh1, float* dx) {
-    dgrad_all<float>(E, H, F, offsets, dy, h1, w1, w2, dh1, dx);
+    dgrad_all<float>(E, H, F, offsets, ACT_SWIGLU, nullptr, dy, h1, w1, w2, dh1, dx, nullptr);
 }
 
 // The same two passes in fp64 without rounding (finite-difference tests).
 void oracle_forward_f64(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
                         const double* x, const double* w1, const double* w2,
                         double* h1, double* a, double* y) {
-    forward_all<double>(E, H, F, offsets, x, w1, w2, h1, a, y);
+    forward_all<double>(E, H, F, offsets, ACT_SWIGLU, nullptr, x, w1, w2, h1, a, y);
 }
 
 void oracle_dgrad_f64(int64_t E, int64_t H, int64_t F, const int64_t* offsets,
                       const double* dy, const double* h1, const double* w1, const double* w2,
                       double* dh1, double* dx) {
-    dgrad_all<double>(E, H, F, offsets, dy, h1, w1, w2, dh1, dx);
+    dgrad_all<double>(E, H, F, offsets, ACT_SWIGLU, nullptr, dy, h1, w1, w2, dh1, dx, nullptr);
+}
+
+// Forward and input gradient with the activation chosen by act (0 SwiGLU,
+// 1 QuickGeGLU) and optional per-row probabilities probs [M] (null: none).
+// dprobs [M] (may be null) receives dp_r.
+void oracle_forward_glu_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets, int act,
+                            const float* probs, const float* x, const float* w1, const float* w2,
+                            float* h1, float* a, float* y) {
+    forward_all<float>(E, H, F, offsets, act, probs, x, w1, w2, h1, a, y);
+}
+
+void oracle_dgrad_glu_f32(int64_t E, int64_t H, int64_t F, const int64_t* offsets, int act,
+                          const float* probs, const float* dy, const float* h1, const float* w1,
+                          const float* w2, float* dh1, float* dx, float* dprobs) {
+    dgrad_all<float>(E, H, F, offsets, act, probs, dy, h1, w1, w2, dh1, dx, dprobs);
+}
+
+void oracle_forward_glu_f64(int64_t E, int64_t H, int64_t F, const int64_t* offsets, int act,
+                            const double* probs, const double* x, const double* w1, const double* w2,
+                            double* h1, double* a, double* y) {
+    forward_all<double>(E, H, F, offsets, act, probs, x, w1, w2, h1, a, y);
+}
+
+void oracle_dgrad_glu_f64(int64_t E, int64_t H, int64_t F, const int64_t* offsets, int act,
+                          const double* probs, const double* dy, const double* h1, const double* w1,
+                          const double* w2, double* dh1, double* dx, double* dprobs) {
+    dgrad_all<double>(E, H, F, offsets, act, probs, dy, h1, w1, w2, dh1, dx, dprobs);
 }
 
 }  // extern "C"
