@@ -9,6 +9,11 @@ timed with HIP events on the launch stream) and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+                    [--activation swiglu|qgeglu] [--weighted]
+
+--activation / --weighted time the QuickGeGLU and router-probability-weighted
+variants (gg_forward_fc1_glu + gg_forward_fc2 + gg_dgrad_glu, dprobs
+included); the default line is plain SwiGLU.
 """
 from __future__ import annotations
 
@@ -63,7 +68,7 @@ def load_traffic(workload_name: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, target_s: float):
+def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
     """The CPU oracle, as it stands, on the first k rows of every non-empty
     expert (k calibrated to about target_s seconds of work)."""
     import numpy as np
@@ -85,8 +90,13 @@ def cpu_baseline(case, target_s: float):
         xs = case.x[torch.from_numpy(rows)]
         dys = case.dy[torch.from_numpy(rows)]
         t0 = time.perf_counter()
-        fw = oracle.forward(xs, comp, w1, w2)
-        oracle.dgrad(dys, fw["h1"], comp, w1, w2)
+        if act == "swiglu" and probs is None:
+            fw = oracle.forward(xs, comp, w1, w2)
+            oracle.dgrad(dys, fw["h1"], comp, w1, w2)
+        else:
+            pr = None if probs is None else probs[rows]
+            fw = oracle.forward_glu(xs, comp, w1, w2, act, pr)
+            oracle.dgrad_glu(dys, fw["h1"], comp, w1, w2, act, pr)
         return rows.size, time.perf_counter() - t0
 
     # grow the sample until one run takes about target_s (small samples
@@ -192,6 +202,12 @@ def main():
                     help="instead of the benchmark line, compare one grouped launch per GEMM with one "
                          "launch per expert (the same library, E=1 calls) and with a HIP-graph replay "
                          "of the grouped step; prints one JSON line")
+    ap.add_argument("--activation", choices=("swiglu", "qgeglu"), default="swiglu",
+                    help="gated activation of the FC1 epilogue (gg_forward_fc1_glu / gg_dgrad_glu "
+                         "for anything but plain SwiGLU)")
+    ap.add_argument("--weighted", action="store_true",
+                    help="weight the activation by a per-row router probability (fp32, seeded "
+                         "uniform in [0.05, 1)) and return its gradient dprobs from the dgrad")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -232,6 +248,13 @@ def main():
     y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     dx = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    glu = args.activation != "swiglu" or args.weighted
+    probs_np = (np.random.default_rng(w.seed + 17).uniform(0.05, 1.0, M).astype(np.float32)
+                if args.weighted else None)
+    probs = torch.from_numpy(probs_np).to(dev) if args.weighted else None
+    dprobs = torch.empty(M, dtype=torch.float32, device=dev) if args.weighted else None
+    ws_glu = (torch.empty(gg.dgrad_glu_workspace_bytes(M, F, args.weighted), dtype=torch.uint8, device=dev)
+              if glu else None)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -244,13 +267,20 @@ def main():
             e2 = torch.cuda.Event(enable_timing=True)
             e3 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
+        if glu:
+            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a)
+        else:
+            gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
         if record:
             e1.record(stream)
         gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
         if record:
             e2.record(stream)
-        gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
+        if glu:
+            gg.gg_dgrad_glu(dy, h1, off, packed, E, H, F, args.activation, probs,
+                            want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs)
+        else:
+            gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
         if record:
             e3.record(stream)
             ev["fc1"].append((e0, e1))
@@ -293,7 +323,7 @@ def main():
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
         roof = {"kernel": "grouped_gemm_kernel<FC1+SwiGLU>", "bound": "hbm", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
-    roof.update({"traffic": load_traffic(args.workload, "fc1"), "avg_launch_ms": fc1_ms,
+    roof.update({"traffic": None if glu else load_traffic(args.workload, "fc1"), "avg_launch_ms": fc1_ms,
                  "flops_per_launch": fc1_flops, "algorithmic_bytes_per_launch": fc1_bytes})
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -301,7 +331,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "experts": E, "tokens": case.T, "topk": w.topk,
                    "routed_rows": M, "hidden": H, "ffn": F, "routing": w.routing,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "activation": args.activation,
+                   "weighted": bool(args.weighted)},
         "routed_rows_per_s": M / (ms * 1e-3), "tokens_per_s": case.T / (ms * 1e-3),
         "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "hbm_GBps_algorithmic": (bfwd + bdg) / (ms * 1e-3) / 1e9,
@@ -312,7 +343,7 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.activation, probs_np)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -114,6 +114,50 @@ int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
              const void* packed, int64_t E, int64_t H, int64_t F,
              void* workspace, size_t workspace_bytes, void* dx, hipStream_t stream);
 
+/* ---- Weighted SwiGLU / QuickGeGLU (paged-stash pull request, "What does
+ * this PR do" and "Validation": the fused activation is SwiGLU or QuickGeGLU,
+ * and its weighted form takes each routed row's router probability at the
+ * activation boundary).  The pages give no formula; this library reads them as
+ *   act(g) = g * sigmoid(c g),  c = 1 (GG_ACT_SWIGLU) or 1.702 (GG_ACT_QGEGLU)
+ *   A      = bf16(p_r * act(gate) * up)        (probs == NULL: p_r = 1)
+ *   dH1    = [p_r dA up act'(gate) | p_r dA act(gate)]
+ *   dp_r   = sum_j dA[r, j] act(gate[r, j]) up[r, j]   (fp32, not rounded)
+ * with gate, up the bf16 H1 values and dA = bf16(dY W2_e).  The sum of dp_r
+ * is taken in a fixed order (32-column groups in increasing order, each
+ * group in a fixed lane order), so dp_r, like every other output, does not
+ * depend on the rest of the batch. */
+typedef enum {
+    GG_ACT_SWIGLU = 0,
+    GG_ACT_QGEGLU = 1
+} gg_activation;
+
+/* Bytes of the gg_dgrad_glu workspace: dH1 [M][2F] bf16 (4*M*F), plus, when
+ * dp is requested, 4*M*ceil(F/32) bytes of fp32 partial sums. */
+size_t gg_dgrad_glu_workspace_bytes(int64_t M, int64_t F, int with_dprobs);
+
+/* gg_forward_fc1_swiglu with the activation chosen by `activation` (a
+ * gg_activation) and, when `probs` is not NULL, each routed row's activation
+ * scaled by probs[r] (DEVICE fp32 [M], 4-byte aligned, read only).  An
+ * unknown activation gives GG_ERR_INVALID_ARGUMENT.  With GG_ACT_SWIGLU and
+ * probs == NULL the results are those of gg_forward_fc1_swiglu, bit for bit. */
+int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M,
+                       const void* packed, int64_t E, int64_t H, int64_t F,
+                       int activation, const float* probs,
+                       void* h1_out, void* a_out, hipStream_t stream);
+
+/* Input gradient of gg_forward_fc1_glu + gg_forward_fc2: as gg_dgrad, with
+ * the same `activation` and `probs` as the forward.  dprobs (DEVICE fp32 [M],
+ * 4-byte aligned, or NULL) receives dp_r for the routed rows; the workspace
+ * must then hold gg_dgrad_glu_workspace_bytes(M, F, 1) bytes (dH1 first, then
+ * the partial sums).  Two launches on `stream`, three with dprobs.  With
+ * GG_ACT_SWIGLU, probs == NULL and dprobs == NULL the results are those of
+ * gg_dgrad, bit for bit. */
+int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
+                 const void* packed, int64_t E, int64_t H, int64_t F,
+                 int activation, const float* probs,
+                 void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
+                 hipStream_t stream);
+
 /* Diagnostic: round n fp32 values to bf16 on the device with the same
  * conversion the epilogues use (lets a test check the device rounding
  * against round-to-nearest-even).  in: DEVICE float[n]; out: DEVICE

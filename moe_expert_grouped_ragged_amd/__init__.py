@@ -8,6 +8,12 @@ current stream.  The functions carry the C names:
   gg_forward_fc1_swiglu(x, offsets, packed, ...) -> (h1, a)
   gg_forward_fc2(a, offsets, packed, ...)        -> y
   gg_dgrad(dy, h1, offsets, packed, ...)         -> dx  (dH1 left in the workspace)
+  gg_forward_fc1_glu(x, offsets, packed, ..., activation, probs) -> (h1, a)
+  gg_dgrad_glu(dy, h1, offsets, packed, ..., activation, probs)  -> (dx, dprobs)
+
+The *_glu calls add the QuickGeGLU activation and the weighting of the
+activation by each row's router probability (fp32 [M]), with dp of that
+weight from the input gradient.
 
 Frozen, bias-free bf16 expert weights only: the Megatron-LM pull request
 "perf(moe): add frozen grouped GEMM for adapter training" (section "Why
@@ -36,8 +42,13 @@ GG_ERR_WORKSPACE_TOO_SMALL = 4
 GG_ERR_ALIASING = 5
 GG_ERR_HIP = 6
 
+GG_ACT_SWIGLU = 0
+GG_ACT_QGEGLU = 1
+ACTIVATIONS = {"swiglu": GG_ACT_SWIGLU, "qgeglu": GG_ACT_QGEGLU}
+
 EXPORTED = ("gg_status_string", "gg_packed_bytes", "gg_dgrad_workspace_bytes", "gg_pack_weights",
-            "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16")
+            "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16",
+            "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu")
 
 
 def _load() -> ctypes.CDLL:
@@ -57,8 +68,12 @@ def _load() -> ctypes.CDLL:
     lib.gg_forward_fc2.argtypes = [p, p, i64, p, i64, i64, i64, p, p]
     lib.gg_dgrad.argtypes = [p, p, p, i64, p, i64, i64, i64, p, sz, p, p]
     lib.gg_round_bf16.argtypes = [p, p, i64, p]
+    lib.gg_dgrad_glu_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.gg_dgrad_glu_workspace_bytes.restype = sz
+    lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, i64, i64, i64, i32, p, p, p, p]
+    lib.gg_dgrad_glu.argtypes = [p, p, p, i64, p, i64, i64, i64, i32, p, p, sz, p, p, p]
     for name in ("gg_pack_weights", "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad",
-                 "gg_round_bf16"):
+                 "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -213,6 +228,82 @@ def gg_dgrad(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: 
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                         dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad")
     return dx
+
+
+def _activation(activation) -> int:
+    if isinstance(activation, str):
+        if activation not in ACTIVATIONS:
+            raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+        return ACTIVATIONS[activation]
+    return int(activation)
+
+
+def _probs_cuda(probs: Optional[torch.Tensor], M: int, name: str = "probs") -> Optional[torch.Tensor]:
+    if probs is None:
+        return None
+    if probs.dtype != torch.float32 or not probs.is_cuda or probs.shape != (M,) or not probs.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of shape [M]")
+    return probs
+
+
+def dgrad_glu_workspace_bytes(M: int, F: int, with_dprobs: bool) -> int:
+    return int(lib.gg_dgrad_glu_workspace_bytes(M, F, int(bool(with_dprobs))))
+
+
+def gg_forward_fc1_glu(x: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
+                       E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
+                       save_h1: bool = True, h1_out: Optional[torch.Tensor] = None,
+                       a_out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+                       ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """FC1 with the fused activation ("swiglu" | "qgeglu"), optionally scaled
+    per row by probs (float32 [M]) -> (H1 or None, A)."""
+    _bf16_cuda(x, "x")
+    _bf16_cuda(packed, "packed")
+    M = x.shape[0]
+    if x.shape != (M, H):
+        raise ValueError("x must be [M, H]")
+    off = _offsets(offsets, E)
+    pr = _probs_cuda(probs, M)
+    if a_out is None:
+        a_out = torch.empty(M, F, dtype=torch.bfloat16, device=x.device)
+    if h1_out is None and save_h1:
+        h1_out = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=x.device)
+    _check(lib.gg_forward_fc1_glu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+                                  _activation(activation), _ptr(pr), _ptr(h1_out), a_out.data_ptr(),
+                                  _stream_ptr(stream)), "gg_forward_fc1_glu")
+    return h1_out, a_out
+
+
+def gg_dgrad_glu(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
+                 E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
+                 want_dprobs: bool = True, workspace: Optional[torch.Tensor] = None,
+                 dx: Optional[torch.Tensor] = None, dprobs: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Input gradient of gg_forward_fc1_glu + FC2 -> (dx, dprobs or None).
+    The workspace (a byte buffer of dgrad_glu_workspace_bytes) keeps dH1 [M, 2F]
+    bf16 at its start."""
+    _bf16_cuda(dy, "dy")
+    _bf16_cuda(h1, "h1")
+    _bf16_cuda(packed, "packed")
+    M = dy.shape[0]
+    if dy.shape != (M, H) or h1.shape != (M, 2 * F):
+        raise ValueError("dy must be [M, H] and h1 [M, 2F]")
+    off = _offsets(offsets, E)
+    pr = _probs_cuda(probs, M)
+    if dprobs is None and want_dprobs:
+        dprobs = torch.empty(M, dtype=torch.float32, device=dy.device)
+    dprobs = _probs_cuda(dprobs, M, "dprobs")
+    if workspace is None:
+        workspace = torch.empty(dgrad_glu_workspace_bytes(M, F, dprobs is not None), dtype=torch.uint8,
+                                device=dy.device)
+    if dx is None:
+        dx = torch.empty(M, H, dtype=torch.bfloat16, device=dy.device)
+    _check(lib.gg_dgrad_glu(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+                            _activation(activation), _ptr(pr), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
+                            _stream_ptr(stream)), "gg_dgrad_glu")
+    return dx, dprobs
 
 
 def gg_round_bf16(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:

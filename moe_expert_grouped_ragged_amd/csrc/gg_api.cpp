@@ -120,8 +120,22 @@ gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed
     p.w_expert_stride = 3 * F * H;
     p.w = static_cast<const uint16_t*>(packed);
     p.up_off = static_cast<int>(F);
+    p.slope = 1.0f;
     return p;
 }
+
+// Slope of the gate activation's sigmoid, or 0 for an unknown activation.
+float act_slope(int activation) {
+    switch (activation) {
+        case GG_ACT_SWIGLU: return 1.0f;
+        case GG_ACT_QGEGLU: return 1.702f;
+        default: return 0.0f;
+    }
+}
+
+int64_t dp_groups(int64_t F) { return (F + 31) / 32; }
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 }  // namespace
 
@@ -149,6 +163,13 @@ size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F) {
 size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F) {
     if (M <= 0 || F <= 0) return 0;
     return static_cast<size_t>(4) * static_cast<size_t>(M) * static_cast<size_t>(F);
+}
+
+size_t gg_dgrad_glu_workspace_bytes(int64_t M, int64_t F, int with_dprobs) {
+    if (M <= 0 || F <= 0) return 0;
+    size_t n = gg_dgrad_workspace_bytes(M, F);
+    if (with_dprobs) n += static_cast<size_t>(4) * static_cast<size_t>(M) * static_cast<size_t>(dp_groups(F));
+    return n;
 }
 
 int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, const void* const* w2,
@@ -192,15 +213,24 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, cons
 int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M, const void* packed,
                           int64_t E, int64_t H, int64_t F, void* h1_out, void* a_out,
                           hipStream_t stream) {
+    return gg_forward_fc1_glu(x, offsets, M, packed, E, H, F, GG_ACT_SWIGLU, nullptr, h1_out, a_out, stream);
+}
+
+int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const void* packed, int64_t E,
+                       int64_t H, int64_t F, int activation, const float* probs, void* h1_out, void* a_out,
+                       hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
+    const float slope = act_slope(activation);
+    if (slope == 0.0f) return GG_ERR_INVALID_ARGUMENT;
     if (M == 0) return GG_OK;
     if (!x || !offsets || !packed || !a_out) return GG_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(packed) || !aligned16(a_out) || (h1_out && !aligned16(h1_out)) ||
-        (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        (reinterpret_cast<uintptr_t>(offsets) & 7u) || (probs && !aligned4(probs)))
         return GG_ERR_MISALIGNED;
     std::vector<Range> ins = {range_of(x, M * H * 2), range_of(packed, gg_packed_bytes(E, H, F)),
                               range_of(offsets, (E + 1) * 8)};
+    if (probs) ins.push_back(range_of(probs, M * 4));
     std::vector<Range> outs = {range_of(a_out, M * F * 2)};
     if (h1_out) outs.push_back(range_of(h1_out, M * 2 * F * 2));
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
@@ -214,6 +244,8 @@ int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M, cons
     p.ldw = static_cast<int>(H);
     p.out0 = static_cast<uint16_t*>(a_out);
     p.out1 = static_cast<uint16_t*>(h1_out);
+    p.slope = slope;
+    p.probs = probs;
     return gg::launch_fc1_swiglu(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
@@ -245,18 +277,30 @@ int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void*
 int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
              int64_t E, int64_t H, int64_t F, void* workspace, size_t workspace_bytes, void* dx,
              hipStream_t stream) {
+    return gg_dgrad_glu(dy, h1, offsets, M, packed, E, H, F, GG_ACT_SWIGLU, nullptr, workspace, workspace_bytes,
+                        dx, nullptr, stream);
+}
+
+int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
+                 int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
+                 size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
+    const float slope = act_slope(activation);
+    if (slope == 0.0f) return GG_ERR_INVALID_ARGUMENT;
     if (M == 0) return GG_OK;
     if (!dy || !h1 || !offsets || !packed || !workspace || !dx) return GG_ERR_INVALID_ARGUMENT;
     if (!aligned16(dy) || !aligned16(h1) || !aligned16(packed) || !aligned16(workspace) ||
-        !aligned16(dx) || (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        !aligned16(dx) || (reinterpret_cast<uintptr_t>(offsets) & 7u) || (probs && !aligned4(probs)) ||
+        (dprobs && !aligned4(dprobs)))
         return GG_ERR_MISALIGNED;
-    if (workspace_bytes < gg_dgrad_workspace_bytes(M, F)) return GG_ERR_WORKSPACE_TOO_SMALL;
+    const size_t ws_need = gg_dgrad_glu_workspace_bytes(M, F, dprobs != nullptr);
+    if (workspace_bytes < ws_need) return GG_ERR_WORKSPACE_TOO_SMALL;
     std::vector<Range> ins = {range_of(dy, M * H * 2), range_of(h1, M * 2 * F * 2),
                               range_of(packed, gg_packed_bytes(E, H, F)), range_of(offsets, (E + 1) * 8)};
-    std::vector<Range> outs = {range_of(workspace, gg_dgrad_workspace_bytes(M, F)),
-                               range_of(dx, M * H * 2)};
+    if (probs) ins.push_back(range_of(probs, M * 4));
+    std::vector<Range> outs = {range_of(workspace, ws_need), range_of(dx, M * H * 2)};
+    if (dprobs) outs.push_back(range_of(dprobs, M * 4));
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
     DeviceInfo info;
     if ((st = device_info(stream, &info)) != GG_OK) return st;
@@ -270,7 +314,18 @@ int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, 
     p.ldw = static_cast<int>(F);
     p.aux = static_cast<const uint16_t*>(h1);
     p.out0 = static_cast<uint16_t*>(workspace);
+    p.slope = slope;
+    p.probs = probs;
+    // dp partial sums [M][ceil(F/32)] fp32 after dH1 in the workspace
+    float* dp_part = dprobs ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                       gg_dgrad_workspace_bytes(M, F))
+                            : nullptr;
+    p.dp_part = dp_part;
+    p.dp_ld = static_cast<int>(dp_groups(F));
     if (gg::launch_dgrad_fc2(p, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
+    if (dprobs && gg::launch_dp_reduce(offsets, static_cast<int>(E), static_cast<int>(M), dp_part,
+                                       static_cast<int>(dp_groups(F)), dprobs, stream) != hipSuccess)
+        return GG_ERR_HIP;
     // dX = dH1 W1_e
     gg::GemmParams q = base_params(offsets, M, packed, E, H, F);
     q.act = static_cast<const uint16_t*>(workspace);

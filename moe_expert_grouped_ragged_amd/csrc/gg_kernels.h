@@ -25,6 +25,13 @@ struct GemmParams {
     uint16_t* out0;            // Y / dX, or A (SwiGLU), or dH1 [M][2F] (SwiGLU derivative)
     uint16_t* out1;            // SwiGLU: H1 [M][2F] or null
     const uint16_t* aux;       // SwiGLU derivative: saved H1 [M][2F]
+    // Gated activation act(g) = g * sigmoid(slope * g): slope 1 is SwiGLU,
+    // 1.702 QuickGeGLU.
+    float slope;
+    const float* probs;        // per-row weight of the activation [M], or null
+    float* dp_part;            // derivative variant: partial sums of dp per row and
+                               // 32-column group [M][dp_ld], or null
+    int dp_ld;                 // ceil(N / 32)
 };
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
@@ -32,5 +39,8 @@ hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+// dprobs[r] = sum over g of part[r][g] in increasing g, for the routed rows.
+hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
+                            hipStream_t s);
 
 }  // namespace gg

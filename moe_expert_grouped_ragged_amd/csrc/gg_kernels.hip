@@ -243,9 +243,15 @@ constexpr int B_PW = B_STAGE * 2 / 1024 / NWAVES;
 constexpr int LPS = A_PW + B_PW;                                // per wave per stage
 static_assert(A_PW * NWAVES * 1024 == A_STAGE * 2 && B_PW * NWAVES * 1024 == B_STAGE * 2, "DMA split");
 
-template <bool W_KN, int EPI>
+// EXT selects the activation options (QuickGeGLU slope, per-row weights, dp
+// partial sums).  Without it they fold to plain SwiGLU, so the plain
+// instantiations carry none of their registers.
+template <bool W_KN, int EPI, bool EXT>
 __global__ __launch_bounds__(NTHREADS)
 void grouped_gemm_kernel(const GemmParams p) {
+    const float slope = EXT ? p.slope : 1.0f;
+    const float* const probs = EXT ? p.probs : nullptr;
+    float* const dp_part = EXT ? p.dp_part : nullptr;
     // Operand stages: NSTAGE token panels, then NSTAGE weight panels (the
     // streaming flavor lays its own stages over the same bytes).
     __shared__ __attribute__((aligned(1024))) uint16_t s_buf[NSTAGE * (A_STAGE + B_STAGE)];
@@ -612,6 +618,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                         }
                     }
                 } else if constexpr (EPI == EPI_SWIGLU) {
+                    const float pr = (probs && rv) ? probs[grow] : 1.0f;
 #pragma unroll
                     for (int g = 0; g < 2; ++g) {
                         const int f = it.col0 + wave * 16 + 8 * g + 4 * (lane >> 5);
@@ -622,7 +629,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                             ub[x] = f2bf(sacc[b][4 * g + 8 + x]);
                             const float gg = bf2f(gb[x]);
                             const float uu = bf2f(ub[x]);
-                            ab[x] = f2bf(gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu);
+                            const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
+                            ab[x] = f2bf(probs ? pr * v : v);
                         }
                         if (rv && f < N) {
                             *reinterpret_cast<uint2*>(p.out0 + grow * N + f) =
@@ -635,6 +643,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                         }
                     }
                 } else {
+                    const float pr = (probs && rv) ? probs[grow] : 1.0f;
+                    float dps = 0.0f;   // this lane's share of dp over the wave's 32 columns
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int f = it.col0 + wave * 32 + 8 * g + 4 * (lane >> 5);
@@ -650,14 +660,22 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 const float gg = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
                                 const float uu = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
                                 const float da = bf2f(f2bf(sacc[b][4 * g + x]));
-                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
-                                dg[x] = da * uu * sgm * (1.0f + gg * (1.0f - sgm));
-                                du[x] = da * gg * sgm;
+                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg)));
+                                const float dap = probs ? pr * da : da;
+                                dg[x] = dap * uu * sgm * (1.0f + slope * gg * (1.0f - sgm));
+                                du[x] = dap * gg * sgm;
+                                dps += da * (gg * sgm * uu);
                             }
                             uint16_t* dh = p.out0 + grow * (2 * N) + f;
                             *reinterpret_cast<uint2*>(dh) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
                             *reinterpret_cast<uint2*>(dh + N) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
                         }
+                    }
+                    if (dp_part) {
+                        // lanes l and l + 32 hold the two halves of the row's 32 columns
+                        const float tot = dps + __shfl_xor(dps, 32, 64);
+                        const int c0 = it.col0 + wave * 32;
+                        if (lane < 32 && rv && c0 < N) dp_part[grow * p.dp_ld + c0 / 32] = tot;
                     }
                 }
             }
@@ -824,6 +842,8 @@ void grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
                     const int i = pass * 2 + ii;
+                    const int prow = wrow0 + pass * 64 + ii * 32 + (lane & 31);
+                    const float pr = (probs && prow < c_row_end) ? probs[prow] : 1.0f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int r = ii * 32 + (lane & 31);
@@ -836,8 +856,9 @@ void grouped_gemm_kernel(const GemmParams p) {
                             ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
                             const float g = bf2f(gb[x]);
                             const float uu = bf2f(ub[x]);
-                            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                            ab[x] = f2bf(sg * uu);
+                            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
+                            const float v = sg * uu;
+                            ab[x] = f2bf(probs ? pr * v : v);
                         }
                         *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
                         *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
@@ -900,12 +921,18 @@ void grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
                     const int i = pass * 2 + ii;
+                    const int prow = prow0 + ii * 32 + (lane & 31);
+                    const float pr = (probs && prow < c_row_end) ? probs[prow] : 1.0f;
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
+                    for (int j = 0; j < FN; ++j) {
+                        // fragment j: output columns gc0 .. gc0 + 31
+                        const int gc0 = c_col0 + j * (TBN / 2) + wq * 32;
+                        float dps = 0.0f;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int r = ii * 32 + (lane & 31);
                             const int col = j * 32 + q * 8 + (lane >> 5) * 4;    // 4 columns
+                            const bool cv = gc0 + q * 8 + (lane >> 5) * 4 < N;
                             const int off = r * 64 + (((col >> 3) ^ ((r >> 1) & 7)) << 3) + (col & 7);
                             const uint2 hg = *reinterpret_cast<const uint2*>(sG + off);
                             const uint2 hu = *reinterpret_cast<const uint2*>(sU + off);
@@ -919,15 +946,24 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 const float g = bf2f(gbits);
                                 const float u = bf2f(ubits);
                                 const float da = bf2f(f2bf(acc_rd(acc[i][j][q * 4 + x])));
-                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                                dg[x] = da * u * sgm * (1.0f + g * (1.0f - sgm));
-                                du[x] = da * g * sgm;
+                                const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
+                                const float dap = probs ? pr * da : da;
+                                dg[x] = dap * u * sgm * (1.0f + slope * g * (1.0f - sgm));
+                                du[x] = dap * g * sgm;
+                                if (cv) dps += da * (g * sgm * u);
                             }
                             *reinterpret_cast<uint2*>(sG + off) =
                                 make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
                             *reinterpret_cast<uint2*>(sU + off) =
                                 make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
                         }
+                        if (dp_part) {
+                            // same per-lane order and halves as the streaming flavor
+                            const float tot = dps + __shfl_xor(dps, 32, 64);
+                            if (lane < 32 && prow < c_row_end && gc0 < N)
+                                dp_part[static_cast<int64_t>(prow) * p.dp_ld + gc0 / 32] = tot;
+                        }
+                    }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -965,9 +1001,25 @@ __global__ void round_bf16_kernel(const float* __restrict__ in, uint16_t* __rest
         out[i] = f2bf(in[i]);
 }
 
+// dp of every routed row: the partial sums of its 32-column groups added in
+// group order (the same order whichever flavor produced them).
+__global__ void dp_reduce_kernel(const int64_t* __restrict__ offsets, int E, int M, const float* __restrict__ part,
+                                 int ld, float* __restrict__ dprobs) {
+    int64_t lo = offsets[0], hi = offsets[E];
+    lo = lo < 0 ? 0 : (lo > M ? M : lo);
+    hi = hi < lo ? lo : (hi > M ? M : hi);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t r = lo + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < hi; r += stride) {
+        const float* pr = part + r * ld;
+        float s = 0.0f;
+        for (int g = 0; g < ld; ++g) s += pr[g];
+        dprobs[r] = s;
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
-template <bool W_KN, int EPI>
+template <bool W_KN, int EPI, bool EXT>
 static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream) {
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int64_t tiles_n = (p.N + TILE_COLS - 1) / TILE_COLS;
@@ -977,22 +1029,35 @@ static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream
     int64_t grid = num_cu;            // one workgroup per CU (LDS-limited)
     if (upper < grid) grid = upper;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((grouped_gemm_kernel<W_KN, EPI>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
+    hipLaunchKernelGGL((grouped_gemm_kernel<W_KN, EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(NTHREADS), 0,
                        stream, p);
     return hipGetLastError();
 }
 
+static bool plain_swiglu(const GemmParams& p) { return p.slope == 1.0f && !p.probs && !p.dp_part; }
+
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<false, EPI_SWIGLU>(p, num_cu, s);
+    return plain_swiglu(p) ? launch_cfg<false, EPI_SWIGLU, false>(p, num_cu, s)
+                           : launch_cfg<false, EPI_SWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<false, EPI_STORE>(p, num_cu, s);
+    return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
 }
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<true, EPI_DSWIGLU>(p, num_cu, s);
+    return plain_swiglu(p) ? launch_cfg<true, EPI_DSWIGLU, false>(p, num_cu, s)
+                           : launch_cfg<true, EPI_DSWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<true, EPI_STORE>(p, num_cu, s);
+    return launch_cfg<true, EPI_STORE, false>(p, num_cu, s);
+}
+hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
+                            hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    int64_t blocks = (static_cast<int64_t>(M) + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(dp_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, offsets, E, M, part,
+                       ld, dprobs);
+    return hipGetLastError();
 }
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;

@@ -96,3 +96,24 @@ def stagewise(x, dy, offsets, w1, w2, h1, a, y, dh1, dx, rows=None) -> list:
             check("dx", dx, oracle.dgrad_fc1(dh1c, offsets, w1), rows),
             check_chained("dx_chained", dx, dg["dx"], rows)]
     return out
+
+
+def stagewise_glu(x, dy, offsets, w1, w2, act, probs, h1, a, y, dh1, dx, dprobs, rows=None) -> list:
+    """stagewise() for the weighted SwiGLU / QuickGeGLU passes; probs is the
+    fp32 [M] weight (numpy or None) and dprobs the GPU's fp32 [M] gradient of
+    it, compared per element with the oracle fed the GPU's H1."""
+    import oracle
+    h1c, ac, dh1c = h1.cpu(), a.cpu(), dh1.cpu()
+    fw = oracle.forward_glu(x, offsets, w1, w2, act, probs)
+    out = [check("h1", h1, fw["h1"], rows),
+           check("a", a, oracle.glu(h1c, offsets, act, probs), rows),
+           check("y", y, oracle.fc2(ac, offsets, w2), rows),
+           check_chained("a_chained", a, fw["a"], rows),
+           check_chained("y_chained", y, fw["y"], rows)]
+    dg = oracle.dgrad_glu(dy, h1c, offsets, w1, w2, act, probs)
+    out += [check("dh1", dh1, dg["dh1"], rows, elem_rel=DH1_ELEM_REL),
+            check("dx", dx, oracle.dgrad_fc1(dh1c, offsets, w1), rows),
+            check_chained("dx_chained", dx, dg["dx"], rows)]
+    if dprobs is not None:
+        out.append(check("dprobs", dprobs.detach().cpu().numpy().astype(np.float64), dg["dprobs"], rows))
+    return out

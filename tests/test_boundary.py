@@ -106,6 +106,36 @@ def test_validation_before_any_hip_call():
     assert L.gg_round_bf16(base, base + 2 ** 30, -1, None) == INV
 
 
+def test_glu_entry_points_validate_before_any_hip_call():
+    gg = _gg()
+    L = gg.lib
+    INV, MIS, WS, ALI = (gg.GG_ERR_INVALID_ARGUMENT, gg.GG_ERR_MISALIGNED,
+                         gg.GG_ERR_WORKSPACE_TOO_SMALL, gg.GG_ERR_ALIASING)
+    base = 1 << 40
+    M, H, F = 8, 64, 136
+    x, off, pk, h1, a = base, base + 2 ** 30, base + 2 ** 31, base + 2 ** 32, base + 2 ** 33
+    probs = base + 2 ** 34
+    # the workspace sizes: dH1, then ceil(F/32) fp32 partial sums per row when dp is wanted
+    assert gg.dgrad_glu_workspace_bytes(M, F, False) == 4 * M * F
+    assert gg.dgrad_glu_workspace_bytes(M, F, True) == 4 * M * F + 4 * M * 5
+    # empty batch and unknown activation (checked first)
+    assert L.gg_forward_fc1_glu(None, None, 0, None, 4, H, F, 0, None, None, None, None) == 0
+    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 2, None, h1, a, None) == INV
+    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, -1, None, h1, a, None) == INV
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 7, None, a, 1 << 20, base + 2 ** 35, None, None) == INV
+    # probs / dprobs must be 4-byte aligned
+    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 1, probs + 2, h1, a, None) == MIS
+    ws, dx, dp = base + 2 ** 35, base + 2 ** 36, base + 2 ** 37
+    need = gg.dgrad_glu_workspace_bytes(M, F, True)
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 1, probs, ws, need, dx, dp + 1, None) == MIS
+    # the workspace must hold the partial sums when dprobs is given
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 1, probs, ws, need - 4, dx, dp, None) == WS
+    # aliasing: probs is an input, dprobs an output
+    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 0, a + 8, h1, a, None) == ALI
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 0, probs, ws, need, dx, ws + need - 4, None) == ALI
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 0, probs, ws, need, dx, probs, None) == ALI
+
+
 def test_python_binding_refuses_unsupported_weights():
     gg = _gg()
     import torch

@@ -7,7 +7,9 @@ expert, shifted by row counts that are not multiples of 32 (so the rows land
 in other MFMA lanes), in another expert slot, and beside other experts.  Both
 flavors accumulate the same MFMA k-steps in the same order into fp32
 accumulators that start at zero, and share the epilogue arithmetic, so H1, A,
-Y, dH1 and dX of those rows must be bitwise equal in every batch."""
+Y, dH1 and dX of those rows must be bitwise equal in every batch.  The same holds for the weighted QuickGeGLU path, dprobs
+included: its per-row sum is taken per 32-column group in the same lane order
+by both flavors, then over the groups in order."""
 import numpy as np
 import pytest
 import torch
@@ -34,8 +36,9 @@ def _layouts(R):
     }
 
 
-def _run(layout, R, base):
-    xs, dys, counts, w1s, w2s = [], [], [], [], []
+def _run(layout, R, base, weighted=False):
+    xs, dys, counts, w1s, w2s, ps = [], [], [], [], [], []
+    allp = torch.from_numpy(np.random.default_rng(77).uniform(0.05, 1.0, base.x.shape[0]).astype(np.float32))
     other = 0
     where = None
     for slot in layout:
@@ -44,9 +47,10 @@ def _run(layout, R, base):
         for kind, n in slot:
             if kind == "R":
                 where = sum(counts) + n_slot
-                xs.append(base.x[:R]); dys.append(base.dy[:R])
+                xs.append(base.x[:R]); dys.append(base.dy[:R]); ps.append(allp[:R])
             else:
                 xs.append(base.x[R + other:R + other + n]); dys.append(base.dy[R + other:R + other + n])
+                ps.append(allp[R + other:R + other + n])
                 other += n
             n_slot += n
         counts.append(n_slot)
@@ -59,27 +63,41 @@ def _run(layout, R, base):
     case = workload.Case("invariance", len(counts), base.H, base.F, int(counts.sum()), counts, off,
                          torch.stack(w1s), torch.stack(w2s), x, dy)
     dc = DeviceCase(case)
-    h1, a, y = dc.forward()
-    dh1, dx = dc.dgrad(h1)
-    torch.cuda.synchronize()
     sl = slice(where, where + R)
+    if not weighted:
+        h1, a, y = dc.forward()
+        dh1, dx = dc.dgrad(h1)
+        torch.cuda.synchronize()
+        return {"h1": h1[sl].cpu(), "a": a[sl].cpu(), "y": y[sl].cpu(), "dh1": dh1[sl].cpu(),
+                "dx": dx[sl].cpu()}
+    gg = dc.gg
+    probs = torch.cat(ps).to(dc.dev)
+    h1, a = gg.gg_forward_fc1_glu(dc.x, dc.offsets, dc.packed, dc.E, dc.H, dc.F, "qgeglu", probs)
+    y = gg.gg_forward_fc2(a, dc.offsets, dc.packed, dc.E, dc.H, dc.F)
+    ws = torch.empty(gg.dgrad_glu_workspace_bytes(dc.M, dc.F, True), dtype=torch.uint8, device=dc.dev)
+    dx, dprobs = gg.gg_dgrad_glu(dc.dy, h1, dc.offsets, dc.packed, dc.E, dc.H, dc.F, "qgeglu", probs,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    dh1 = ws[:4 * dc.M * dc.F].view(torch.bfloat16).view(dc.M, 2 * dc.F)
     return {"h1": h1[sl].cpu(), "a": a[sl].cpu(), "y": y[sl].cpu(), "dh1": dh1[sl].cpu(),
-            "dx": dx[sl].cpu()}
+            "dx": dx[sl].cpu(), "dprobs": dprobs[sl].cpu()}
 
 
+@pytest.mark.parametrize("weighted", [False, True], ids=["swiglu", "weighted_qgeglu"])
 @pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64)])
-def test_rows_are_batch_invariant(H, F, R):
+def test_rows_are_batch_invariant(H, F, R, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     base = workload.custom_case([R, 700], H, F, seed=31)
     ref = None
     for name, layout in _layouts(R).items():
         log(f"[invariance] H={H} F={F} R={R} {name}")
-        got = _run(layout, R, base)
+        got = _run(layout, R, base, weighted)
         if ref is None:
             ref = got
             continue
         for k in ref:
-            same = got[k].view(torch.int16) == ref[k].view(torch.int16)
+            same = got[k].view(torch.int32 if k == "dprobs" else torch.int16) == \
+                ref[k].view(torch.int32 if k == "dprobs" else torch.int16)
             assert bool(same.all()), (name, k, int((~same).sum()))
     log(f"[invariance] H={H} F={F} R={R}: every layout bitwise equal to 'alone'")
