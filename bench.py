@@ -9,11 +9,13 @@ timed with HIP events on the launch stream) and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
-                    [--activation swiglu|qgeglu] [--weighted]
+                    [--activation swiglu|qgeglu] [--weighted] [--recompute]
 
 --activation / --weighted time the QuickGeGLU and router-probability-weighted
 variants (gg_forward_fc1_glu + gg_forward_fc2 + gg_dgrad_glu, dprobs
-included); the default line is plain SwiGLU.
+included); --recompute keeps no H1 and recomputes FC1 inside the dgrad call
+(gg_dgrad_recompute; the step's counted work stays 12*M*H*F).  The default
+line is plain SwiGLU with a saved H1.
 """
 from __future__ import annotations
 
@@ -208,6 +210,9 @@ def main():
     ap.add_argument("--weighted", action="store_true",
                     help="weight the activation by a per-row router probability (fp32, seeded "
                          "uniform in [0.05, 1)) and return its gradient dprobs from the dgrad")
+    ap.add_argument("--recompute", action="store_true",
+                    help="forward without saving H1 and input gradient through gg_dgrad_recompute "
+                         "(FC1 recomputed from X inside the dgrad call)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -248,7 +253,7 @@ def main():
     y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     dx = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
-    glu = args.activation != "swiglu" or args.weighted
+    glu = args.activation != "swiglu" or args.weighted or args.recompute
     probs_np = (np.random.default_rng(w.seed + 17).uniform(0.05, 1.0, M).astype(np.float32)
                 if args.weighted else None)
     probs = torch.from_numpy(probs_np).to(dev) if args.weighted else None
@@ -267,7 +272,9 @@ def main():
             e2 = torch.cuda.Event(enable_timing=True)
             e3 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if glu:
+        if args.recompute:
+            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, save_h1=False, a_out=a)
+        elif glu:
             gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a)
         else:
             gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
@@ -276,7 +283,10 @@ def main():
         gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
         if record:
             e2.record(stream)
-        if glu:
+        if args.recompute:
+            gg.gg_dgrad_recompute(dy, x, off, packed, E, H, F, args.activation, probs,
+                                  want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs)
+        elif glu:
             gg.gg_dgrad_glu(dy, h1, off, packed, E, H, F, args.activation, probs,
                             want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs)
         else:
@@ -332,7 +342,7 @@ def main():
         "config": {"workload": args.workload, "experts": E, "tokens": case.T, "topk": w.topk,
                    "routed_rows": M, "hidden": H, "ffn": F, "routing": w.routing,
                    "parallelism": "single-gpu", "activation": args.activation,
-                   "weighted": bool(args.weighted)},
+                   "weighted": bool(args.weighted), "recompute_fc1_in_dgrad": bool(args.recompute)},
         "routed_rows_per_s": M / (ms * 1e-3), "tokens_per_s": case.T / (ms * 1e-3),
         "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "hbm_GBps_algorithmic": (bfwd + bdg) / (ms * 1e-3) / 1e9,

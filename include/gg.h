@@ -158,6 +158,26 @@ int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t
                  void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
                  hipStream_t stream);
 
+/* Input gradient without a saved H1: recomputes FC1 from x (the forward's
+ * input, [M][H]) inside the call, for a forward run with h1_out == NULL.
+ * This is the trade of selective `expert_fc1_act` recompute (Megatron-LM
+ * pull request "perf(moe): add frozen grouped GEMM for adapter training",
+ * section "Scope deliberately omitted"; issue "feat(moe+ssm): expert-LoRA
+ * GEMM stack and hybrid-recompute guard", section "What's in it"): 4*M*F
+ * bytes of H1 are not kept between the forward and the backward, at the
+ * price of 4*M*H*F more FLOPs here.  Three launches on `stream` (four with dprobs):
+ * H1 = X W1_e^T into the workspace, then dA and the activation derivative
+ * overwrite it in place with dH1, then dX.  The workspace size is
+ * gg_dgrad_glu_workspace_bytes(M, F, dprobs != NULL), the same as with a
+ * saved H1.  The recomputed H1 is bit-identical to the forward's, so dx and
+ * dprobs equal those of gg_dgrad_glu with the saved H1, bit for bit.
+ * Other arguments as gg_dgrad_glu. */
+int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, int64_t M,
+                       const void* packed, int64_t E, int64_t H, int64_t F,
+                       int activation, const float* probs,
+                       void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
+                       hipStream_t stream);
+
 /* Diagnostic: round n fp32 values to bf16 on the device with the same
  * conversion the epilogues use (lets a test check the device rounding
  * against round-to-nearest-even).  in: DEVICE float[n]; out: DEVICE

@@ -10,6 +10,8 @@ current stream.  The functions carry the C names:
   gg_dgrad(dy, h1, offsets, packed, ...)         -> dx  (dH1 left in the workspace)
   gg_forward_fc1_glu(x, offsets, packed, ..., activation, probs) -> (h1, a)
   gg_dgrad_glu(dy, h1, offsets, packed, ..., activation, probs)  -> (dx, dprobs)
+  gg_dgrad_recompute(dy, x, offsets, packed, ...)                 -> (dx, dprobs)
+        (no saved H1: FC1 is recomputed from x inside the call)
 
 The *_glu calls add the QuickGeGLU activation and the weighting of the
 activation by each row's router probability (fp32 [M]), with dp of that
@@ -48,7 +50,7 @@ ACTIVATIONS = {"swiglu": GG_ACT_SWIGLU, "qgeglu": GG_ACT_QGEGLU}
 
 EXPORTED = ("gg_status_string", "gg_packed_bytes", "gg_dgrad_workspace_bytes", "gg_pack_weights",
             "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16",
-            "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu")
+            "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute")
 
 
 def _load() -> ctypes.CDLL:
@@ -72,8 +74,9 @@ def _load() -> ctypes.CDLL:
     lib.gg_dgrad_glu_workspace_bytes.restype = sz
     lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, i64, i64, i64, i32, p, p, p, p]
     lib.gg_dgrad_glu.argtypes = [p, p, p, i64, p, i64, i64, i64, i32, p, p, sz, p, p, p]
+    lib.gg_dgrad_recompute.argtypes = [p, p, p, i64, p, i64, i64, i64, i32, p, p, sz, p, p, p]
     for name in ("gg_pack_weights", "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad",
-                 "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu"):
+                 "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -303,6 +306,38 @@ def gg_dgrad_glu(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, pack
                             _activation(activation), _ptr(pr), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
                             _stream_ptr(stream)), "gg_dgrad_glu")
+    return dx, dprobs
+
+
+def gg_dgrad_recompute(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
+                       E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
+                       want_dprobs: bool = False, workspace: Optional[torch.Tensor] = None,
+                       dx: Optional[torch.Tensor] = None, dprobs: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Input gradient without a saved H1: FC1 is recomputed from the forward
+    input x [M, H] inside the call -> (dx, dprobs or None).  The workspace
+    ends up holding dH1 [M, 2F] bf16 at its start."""
+    _bf16_cuda(dy, "dy")
+    _bf16_cuda(x, "x")
+    _bf16_cuda(packed, "packed")
+    M = dy.shape[0]
+    if dy.shape != (M, H) or x.shape != (M, H):
+        raise ValueError("dy and x must be [M, H]")
+    off = _offsets(offsets, E)
+    pr = _probs_cuda(probs, M)
+    if dprobs is None and want_dprobs:
+        dprobs = torch.empty(M, dtype=torch.float32, device=dy.device)
+    dprobs = _probs_cuda(dprobs, M, "dprobs")
+    if workspace is None:
+        workspace = torch.empty(dgrad_glu_workspace_bytes(M, F, dprobs is not None), dtype=torch.uint8,
+                                device=dy.device)
+    if dx is None:
+        dx = torch.empty(M, H, dtype=torch.bfloat16, device=dy.device)
+    _check(lib.gg_dgrad_recompute(dy.data_ptr(), x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+                                  _activation(activation), _ptr(pr), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
+                                  _stream_ptr(stream)), "gg_dgrad_recompute")
     return dx, dprobs
 
 

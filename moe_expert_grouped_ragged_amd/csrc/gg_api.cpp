@@ -281,22 +281,29 @@ int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, 
                         dx, nullptr, stream);
 }
 
-int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
-                 int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
-                 size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Input gradient from the saved H1 (h1 != null) or from X, recomputing H1 into
+// the workspace first (x != null; exactly one of the two is given).
+int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* offsets, int64_t M,
+               const void* packed, int64_t E, int64_t H, int64_t F, int activation, const float* probs,
+               void* workspace, size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
     const float slope = act_slope(activation);
     if (slope == 0.0f) return GG_ERR_INVALID_ARGUMENT;
     if (M == 0) return GG_OK;
-    if (!dy || !h1 || !offsets || !packed || !workspace || !dx) return GG_ERR_INVALID_ARGUMENT;
-    if (!aligned16(dy) || !aligned16(h1) || !aligned16(packed) || !aligned16(workspace) ||
+    const void* src = h1 ? h1 : x;   // the saved H1 [M][2F], or X [M][H]
+    if (!dy || !src || !offsets || !packed || !workspace || !dx) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dy) || !aligned16(src) || !aligned16(packed) || !aligned16(workspace) ||
         !aligned16(dx) || (reinterpret_cast<uintptr_t>(offsets) & 7u) || (probs && !aligned4(probs)) ||
         (dprobs && !aligned4(dprobs)))
         return GG_ERR_MISALIGNED;
     const size_t ws_need = gg_dgrad_glu_workspace_bytes(M, F, dprobs != nullptr);
     if (workspace_bytes < ws_need) return GG_ERR_WORKSPACE_TOO_SMALL;
-    std::vector<Range> ins = {range_of(dy, M * H * 2), range_of(h1, M * 2 * F * 2),
+    std::vector<Range> ins = {range_of(dy, M * H * 2), range_of(src, h1 ? M * 2 * F * 2 : M * H * 2),
                               range_of(packed, gg_packed_bytes(E, H, F)), range_of(offsets, (E + 1) * 8)};
     if (probs) ins.push_back(range_of(probs, M * 4));
     std::vector<Range> outs = {range_of(workspace, ws_need), range_of(dx, M * H * 2)};
@@ -305,14 +312,27 @@ int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t
     DeviceInfo info;
     if ((st = device_info(stream, &info)) != GG_OK) return st;
     if ((st = debug_validate_offsets(offsets, E, M, stream)) != GG_OK) return st;
-    // dA = dY W2_e, then the SwiGLU derivative with the saved H1 -> dH1 (workspace)
+    if (!h1) {
+        // recompute H1 = X W1_e^T into the workspace: FC1 as a plain GEMM over
+        // W1's 2F rows (gate | up), the same sums the forward rounds
+        gg::GemmParams r = base_params(offsets, M, packed, E, H, F);
+        r.act = static_cast<const uint16_t*>(x);
+        r.K = static_cast<int>(H);
+        r.N = static_cast<int>(2 * F);
+        r.ldw = static_cast<int>(H);
+        r.out0 = static_cast<uint16_t*>(workspace);
+        if (gg::launch_fc2(r, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
+    }
+    // dA = dY W2_e, then the activation derivative with H1 -> dH1 (workspace;
+    // with a recomputed H1 in place: each H1 element is read only by the lane
+    // that then writes the dH1 element at the same position)
     gg::GemmParams p = base_params(offsets, M, packed, E, H, F);
     p.w = static_cast<const uint16_t*>(packed) + 2 * F * H;
     p.act = static_cast<const uint16_t*>(dy);
     p.K = static_cast<int>(H);
     p.N = static_cast<int>(F);
     p.ldw = static_cast<int>(F);
-    p.aux = static_cast<const uint16_t*>(h1);
+    p.aux = h1 ? static_cast<const uint16_t*>(h1) : static_cast<const uint16_t*>(workspace);
     p.out0 = static_cast<uint16_t*>(workspace);
     p.slope = slope;
     p.probs = probs;
@@ -334,6 +354,26 @@ int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t
     q.ldw = static_cast<int>(H);
     q.out0 = static_cast<uint16_t*>(dx);
     return gg::launch_dgrad_fc1(q, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
+                 int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
+                 size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+    if (M > 0 && !h1) return GG_ERR_INVALID_ARGUMENT;
+    return dgrad_impl(dy, h1, nullptr, offsets, M, packed, E, H, F, activation, probs, workspace,
+                      workspace_bytes, dx, dprobs, stream);
+}
+
+int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, int64_t M, const void* packed,
+                       int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
+                       size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+    if (M > 0 && !x) return GG_ERR_INVALID_ARGUMENT;
+    return dgrad_impl(dy, nullptr, x, offsets, M, packed, E, H, F, activation, probs, workspace,
+                      workspace_bytes, dx, dprobs, stream);
 }
 
 int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
