@@ -153,7 +153,8 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
 // (every row of a small expert, or the tail of a large one), take the
 // weight-streaming flavor: one work item per block of output columns covering
 // all those rows, so each weight byte is read once for them.
-constexpr int SMALL_M = 64;
+constexpr int SMALL_M = 96;
+constexpr int S_BLK = SMALL_M / 32;   // 32-row token blocks of a streaming item
 
 // How an expert with m rows is split: full 256-row tiles, and the rows left
 // over.  A remainder of at most SMALL_M rows (all the rows of a small expert,
@@ -242,6 +243,10 @@ constexpr int A_PW = A_STAGE * 2 / 1024 / NWAVES;               // 1 KiB DMA ins
 constexpr int B_PW = B_STAGE * 2 / 1024 / NWAVES;
 constexpr int LPS = A_PW + B_PW;                                // per wave per stage
 static_assert(A_PW * NWAVES * 1024 == A_STAGE * 2 && B_PW * NWAVES * 1024 == B_STAGE * 2, "DMA split");
+// The streaming flavor's ring (4 stages of 192 weight rows + SMALL_M token
+// rows, 64 k each) lays its stages over the same LDS as the tile stages.
+constexpr int S_RING_EL = 4 * (192 + SMALL_M) * BK;
+constexpr int LDS_BUF_EL = S_RING_EL > NSTAGE * (A_STAGE + B_STAGE) ? S_RING_EL : NSTAGE * (A_STAGE + B_STAGE);
 
 // EXT selects the activation options (QuickGeGLU slope, per-row weights, dp
 // partial sums).  Without it they fold to plain SwiGLU, so the plain
@@ -254,7 +259,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     float* const dp_part = EXT ? p.dp_part : nullptr;
     // Operand stages: NSTAGE token panels, then NSTAGE weight panels (the
     // streaming flavor lays its own stages over the same bytes).
-    __shared__ __attribute__((aligned(1024))) uint16_t s_buf[NSTAGE * (A_STAGE + B_STAGE)];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_buf[LDS_BUF_EL];
     __shared__ int s_off[GG_KMAX_EXPERTS + 1];
     __shared__ int s_pre[GG_KMAX_EXPERTS + 1];
     __shared__ int s_spre[GG_KMAX_EXPERTS + 1];
@@ -480,11 +485,11 @@ void grouped_gemm_kernel(const GemmParams p) {
     // items round-robin.  Per 64-wide K stage the weight panel holds S_ROWS rows
     // (K-contiguous weights; for SwiGLU wave w's 32 rows are 16 gate rows then
     // the matching 16 up rows) or S_ROWS columns (transposed weights), and the
-    // token panel 64 rows (rows past the expert's end repeat its last row).
-    // A 4-stage ring of 32 KiB runs continuously across the items, so the
+    // token panel SMALL_M rows (rows past the expert's end repeat its last row).
+    // A 4-stage ring of 36 KiB runs continuously across the items, so the
     // copies of the next item are in flight while the current one finishes.
-    // Waves w < S_WAVES compute 32 weight rows each against one or two 32-row
-    // token blocks and store the results; the other two waves issue every
+    // Waves w < S_WAVES compute 32 weight rows each against one to S_BLK
+    // 32-row token blocks and store the results; the other two waves issue every
     // copy, so a copy wave's vmcnt counts copies only (vmcnt retires in
     // order: a store queued among the copies would be waited for with them).
     constexpr int SX_EL = SMALL_M * BK;
@@ -500,7 +505,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     // transposed panels [64 k][S_ROWS n]: chunk c of row k at c ^ (2 * (k & 3)),
     // which keeps every chunk inside its aligned group of 8
     auto snc_off = [](int k, int n) { return k * S_ROWS + (((n >> 3) ^ ((k & 3) << 1)) << 3) + (n & 7); };
-    static_assert(S_NST * S_EL <= NSTAGE * (A_STAGE + B_STAGE), "streaming stages fit in LDS");
+    static_assert(S_NST * S_EL <= LDS_BUF_EL, "streaming stages fit in LDS");
     struct SItem { int e, row0, rows, col0; };
     auto stream_items = [&](int t0) -> int {
         const int n_my = (n_stream - t0 + G - 1) / G;
@@ -554,26 +559,28 @@ void grouped_gemm_kernel(const GemmParams p) {
                 dma16(xb, xoff, base + SW_EL * 2 + (cw * SX_PW + i) * 1024);
             }
         };
-        f32x16 sacc[2];
+        f32x16 sacc[S_BLK];
         auto szero = [&]() {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < S_BLK; ++b)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sacc[b][v] = 0.f;
         };
         // K positions >= K (last stage only) are zeroed in the fragments, so
-        // whatever the copies left there never enters a sum.
+        // whatever the copies left there adds nothing (the tile flavor adds the
+        // same zero products).  Every fragment read of the stage is issued
+        // before its MFMAs, so the LDS latency is paid once per stage.
         auto s_mma = [&](int slot_i, int kt, int nblk) {
             const uint16_t* sw = s_buf + slot_i * S_EL;
             const uint16_t* sx = sw + SW_EL;
             const bool last = k_tail && kt == kiters - 1;
+            constexpr int NJ = BK / 16;
+            bf16x8 wf[NJ], xf[NJ][S_BLK];
 #pragma unroll
-            for (int j = 0; j < BK / 16; ++j) {
-                if (last && kt * BK + j * 16 >= K) break;
+            for (int j = 0; j < NJ; ++j) {
                 const int ch = 2 * j + (lane >> 5);
-                bf16x8 wf;
                 if constexpr (!W_KN) {
-                    wf = *reinterpret_cast<const bf16x8*>(sw + kc_off(wave * 32 + (lane & 31), ch));
+                    wf[j] = *reinterpret_cast<const bf16x8*>(sw + kc_off(wave * 32 + (lane & 31), ch));
                 } else {
                     const int g = lane >> 4;
                     const int kb = j * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
@@ -582,19 +589,26 @@ void grouped_gemm_kernel(const GemmParams p) {
                         reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb, n))));
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb + 4, n))));
-                    wf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    wf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-                bf16x8 xf0 = *reinterpret_cast<const bf16x8*>(sx + kc_off(lane & 31, ch));
-                bf16x8 xf1 = xf0;
-                if (nblk > 1) xf1 = *reinterpret_cast<const bf16x8*>(sx + kc_off(32 + (lane & 31), ch));
+#pragma unroll
+                for (int b = 0; b < S_BLK; ++b)
+                    xf[j][b] = (b == 0 || b < nblk)
+                                   ? *reinterpret_cast<const bf16x8*>(sx + kc_off(b * 32 + (lane & 31), ch))
+                                   : xf[j][0];
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
                 if (last && kt * BK + j * 16 + 8 * (lane >> 5) >= K) {
                     const bf16x8 z = {};
-                    wf = z;
-                    xf0 = z;
-                    xf1 = z;
+                    wf[j] = z;
+#pragma unroll
+                    for (int b = 0; b < S_BLK; ++b) xf[j][b] = z;
                 }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf0, sacc[0], 0, 0, 0);
-                if (nblk > 1) sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf1, sacc[1], 0, 0, 0);
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j][0], sacc[0], 0, 0, 0);
+#pragma unroll
+                for (int b = 1; b < S_BLK; ++b)
+                    if (b < nblk) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j][b], sacc[b], 0, 0, 0);
             }
         };
         // Lane holds token (lane & 31) of block b and, for register v, panel row
@@ -602,7 +616,7 @@ void grouped_gemm_kernel(const GemmParams p) {
         auto s_epilogue = [&](const SItem& it, int nblk) {
             mfma_drain();
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < S_BLK; ++b) {
                 if (b >= nblk) break;
                 const int tok = b * 32 + (lane & 31);
                 const bool rv = tok < it.rows;
@@ -708,7 +722,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                 else wait_vmcnt<0>();
             }
             block_barrier();
-            const int nblk = it_c.rows > 32 ? 2 : 1;
+            const int nblk = (it_c.rows + 31) / 32;
             if (s_mma_wave) s_mma(q % S_NST, kt, nblk);
             if (kt == kiters - 1) {
                 if (s_mma_wave) s_epilogue(it_c, nblk);

@@ -84,7 +84,7 @@ def _run(layout, R, base, weighted=False):
 
 
 @pytest.mark.parametrize("weighted", [False, True], ids=["swiglu", "weighted_qgeglu"])
-@pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64)])
+@pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64), (136, 200, 96)])
 def test_rows_are_batch_invariant(H, F, R, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

@@ -85,8 +85,12 @@ def test_tiny_workload():
     # one K stage (H = 64) with one- and two-block streaming items: the
     # accumulators are read right after the last MFMA
     ([5, 0, 7, 33], 64, 64),
-    # around the small-expert (weight-streaming) threshold of 64 rows, K tails
+    # one, two and three 32-row token blocks in streaming items, K tails
     ([31, 32, 63, 64, 65, 0, 1], 136, 200),
+    # around the streaming threshold of 96 rows, for small experts and for the
+    # rows a large expert leaves after its 256-row tiles (1 K stage, one block)
+    ([96, 97, 352, 353, 0, 351, 95], 72, 136),
+    ([95, 96, 97, 0, 609], 64, 64),
     # the maximum expert count: mostly 0..5 rows, one large expert in the middle
     ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 64, 64),
     # many small experts, as in the small-batch workload
