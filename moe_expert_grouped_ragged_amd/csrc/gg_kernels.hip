@@ -7,32 +7,44 @@
 // request, section "Summary"), and then walks the global tile list.  Experts
 // with no rows own no tiles, so their weights are never read.
 //
-// Tile core: bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  Both
-// operand panels stream from HBM straight into LDS with LDS-DMA loads
-// (global_load_lds_dwordx4, 16 bytes per lane) through an NS-stage ring, so
-// several K panels are in flight while the matrix cores work on an earlier
-// one; one barrier per K step.
-//  - K-contiguous panels (tokens; forward weights) sit in LDS as [row][32 k]
-//    with the four 16-byte chunks of a row XOR-swizzled by (row >> 1) & 3;
+// Two flavors share one launch.  Rows that fill 256-row tiles run as 256 x 256
+// output tiles; the at most 96 rows an expert leaves over (all rows of a
+// small expert) run as weight-streaming items, before the tiles.
+//
+// Tile core: bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulators), 8 waves
+// of 128 token rows x 64 output columns.  Both operand panels stream from HBM
+// straight into LDS with LDS-DMA loads (global_load_lds_dwordx4, 16 bytes per
+// lane) through a 2-stage ring of 64-k stages, so the next stage is in flight
+// while the matrix cores work on the current one.
+//  - K-contiguous panels (tokens; forward weights) sit in LDS as [row][64 k]
+//    with the eight 16-byte chunks of a row XOR-swizzled by (row >> 1) & 7;
 //    fragments are read with ds_read_b128.
 //  - The transposed-weight variant (dgrad) reads W as [K][N] (N contiguous):
-//    the panel lands in LDS as [32 k][BN n] with 16-byte chunks swizzled by
-//    2 * (k & 3) and the MFMA operand is assembled with two
+//    the panel lands in LDS as [64 k][256 n] with 16-byte chunks swizzled by
+//    (k & 3) << 2 and the MFMA operand is assembled with two
 //    ds_read_b64_tr_b16 per fragment, which transpose 4x16 blocks of 16-bit
 //    elements across each group of 16 lanes.
+//  - Forward kernels: every wave reads the next k16 step's fragments while
+//    the MFMAs of the current one issue (one barrier per stage).  Dgrad
+//    kernels: the two 4-wave groups alternate ("ping-pong") between reading
+//    and computing 32-k half stages.
 // The weight side is the MFMA "A" operand and the token side the "B"
 // operand, so each lane ends up holding one token row and four groups of
-// four consecutive output columns: stores are 8-byte vectors.
+// four consecutive output columns; epilogues stage results through LDS and
+// store 16-byte row segments.
 //
-// Variants (template parameter EPI and W_KN):
+// Variants (template parameters W_KN, EPI, EXT):
 //   FC1 + SwiGLU  W_KN=false  weights W1_e [2F][H]; a tile loads matching gate
 //                 rows n.. and up rows F+n.. so SwiGLU is applied in
 //                 registers; writes H1 (optional) and A.
-//   FC2           W_KN=false  weights W2_e [H][F]; writes Y.
+//   FC2           W_KN=false  weights W2_e [H][F]; writes Y (also the FC1
+//                 recompute inside the input gradient, over W1's 2F rows).
 //   dgrad FC2     W_KN=true   dA = dY W2_e (contraction over W2's rows); the
 //                 epilogue applies the SwiGLU derivative with the saved H1
 //                 and writes dH1.
 //   dgrad FC1     W_KN=true   dX = dH1 W1_e; writes dX.
+//   EXT           QuickGeGLU slope, per-row weights and dp partial sums in
+//                 the FC1 and dgrad-FC2 epilogues (plain SwiGLU otherwise).
 // Rounding points mirror the unfused computation: H1, A, Y, dA, dH1 and dX
 // are each rounded once to bf16 (round to nearest even); SwiGLU and its
 // derivative read the rounded gate/up and dA.
