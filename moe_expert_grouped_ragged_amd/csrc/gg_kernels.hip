@@ -647,61 +647,93 @@ void grouped_gemm_kernel(const GemmParams p) {
                     if (b < nblk) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j][b], sacc[b], 0, 0, 0);
             }
         };
+        // Item epilogue, staged through the ring slot of the item's last stage:
+        // every wave has finished reading it at the first barrier below, and
+        // the copy waves refill it only after the next stage's barrier.  Per
+        // 32-row token block the compute waves write their results into a
+        // [32][SC] bf16 array (one pad chunk per row), then store whole row
+        // segments with 16-byte stores: scattered 8-byte stores from the
+        // accumulator layout cost several times the write requests per byte.
+        // The derivative variant first copies the block's saved gate|up rows
+        // into the array with LDS-DMA and overwrites them in place.
         // Lane holds token (lane & 31) of block b and, for register v, panel row
         // 8*(v/4) + 4*(lane/32) + v%4 of the wave's 32 rows.
-        auto s_epilogue = [&](const SItem& it, int nblk) {
-            mfma_drain();
+        constexpr int SC = (EPI == EPI_SWIGLU) ? 3 * S_COLS : (EPI == EPI_DSWIGLU ? 2 * S_COLS : S_COLS);
+        constexpr int SCH = SC / 8;             // 16-byte chunks per staged row
+        constexpr int SLD = SC + 8;             // staged row stride in elements
+        constexpr int S_STG_DMA = (32 * (SCH + 1) + 63) / 64;   // derivative: DMA instructions per block
+        static_assert(SC % 8 == 0 && S_STG_DMA * 1024 <= S_EL * 2, "staging fits in a ring slot");
+        auto s_epilogue = [&](const SItem& it, int nblk, int slot_i) {
+            uint16_t* stg = s_buf + slot_i * S_EL;
+            const bool cwave = wave < S_WAVES;
+            block_barrier();                    // every wave is done with the slot
+            if (cwave) mfma_drain();
 #pragma unroll
             for (int b = 0; b < S_BLK; ++b) {
-                if (b >= nblk) break;
+                if (b >= nblk) break;           // nblk is uniform over the workgroup
                 const int tok = b * 32 + (lane & 31);
                 const bool rv = tok < it.rows;
                 const int64_t grow = it.row0 + tok;
-                if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = it.col0 + wave * 32 + 8 * g + 4 * (lane >> 5);
-                        if (rv && col < N) {
-                            const uint2 v = make_uint2(pack2(sacc[b][4 * g], sacc[b][4 * g + 1]),
-                                                       pack2(sacc[b][4 * g + 2], sacc[b][4 * g + 3]));
-                            *reinterpret_cast<uint2*>(p.out0 + grow * N + col) = v;
+                const int r = lane & 31;
+                if constexpr (EPI == EPI_DSWIGLU) {
+                    // saved H1 of the block: gate columns then up columns of each row;
+                    // slots past the rows or columns re-read in-bounds data
+                    if (cwave) {
+                        const uint16_t* hb = p.aux + static_cast<int64_t>(it.row0) * (2 * N);
+                        const uint32_t stg_lds = lds_addr(stg);
+                        for (int ins = wave; ins < S_STG_DMA; ins += S_WAVES) {
+                            const int sl = ins * 64 + lane;
+                            const int sr = min(sl / (SCH + 1), 31);
+                            int sc = sl % (SCH + 1);
+                            if (sc == SCH) sc = 0;
+                            const int arr = sc / (SCH / 2), cc = sc % (SCH / 2);
+                            const int row = min(b * 32 + sr, it.rows - 1);
+                            const int f = min(it.col0 + cc * 8, N - 8);
+                            dma16(hb, static_cast<uint32_t>((row * 2 * N + arr * N + f) * 2), stg_lds + ins * 1024);
                         }
+                        wait_vmcnt<0>();
                     }
-                } else if constexpr (EPI == EPI_SWIGLU) {
-                    const float pr = (probs && rv) ? probs[grow] : 1.0f;
+                    block_barrier();
+                }
+                if (cwave) {
+                    if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-                    for (int g = 0; g < 2; ++g) {
-                        const int f = it.col0 + wave * 16 + 8 * g + 4 * (lane >> 5);
-                        uint32_t gb[4], ub[4], ab[4];
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            gb[x] = f2bf(sacc[b][4 * g + x]);
-                            ub[x] = f2bf(sacc[b][4 * g + 8 + x]);
-                            const float gg = bf2f(gb[x]);
-                            const float uu = bf2f(ub[x]);
-                            const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
-                            ab[x] = f2bf(probs ? pr * v : v);
+                        for (int g = 0; g < 4; ++g) {
+                            const int cl = wave * 32 + 8 * g + 4 * (lane >> 5);
+                            *reinterpret_cast<uint2*>(stg + r * SLD + cl) =
+                                make_uint2(pack2(sacc[b][4 * g], sacc[b][4 * g + 1]),
+                                           pack2(sacc[b][4 * g + 2], sacc[b][4 * g + 3]));
                         }
-                        if (rv && f < N) {
-                            *reinterpret_cast<uint2*>(p.out0 + grow * N + f) =
-                                make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                            if (p.out1) {
-                                uint16_t* h = p.out1 + grow * (2 * N) + f;
-                                *reinterpret_cast<uint2*>(h) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                                *reinterpret_cast<uint2*>(h + N) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                    } else if constexpr (EPI == EPI_SWIGLU) {
+                        const float pr = (probs && rv) ? probs[grow] : 1.0f;
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const int fl = wave * 16 + 8 * g + 4 * (lane >> 5);
+                            uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) {
+                                gb[x] = f2bf(sacc[b][4 * g + x]);
+                                ub[x] = f2bf(sacc[b][4 * g + 8 + x]);
+                                const float gg = bf2f(gb[x]);
+                                const float uu = bf2f(ub[x]);
+                                const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
+                                ab[x] = f2bf(probs ? pr * v : v);
                             }
+                            uint16_t* sr = stg + r * SLD + fl;
+                            *reinterpret_cast<uint2*>(sr) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                            *reinterpret_cast<uint2*>(sr + S_COLS) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                            *reinterpret_cast<uint2*>(sr + 2 * S_COLS) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
                         }
-                    }
-                } else {
-                    const float pr = (probs && rv) ? probs[grow] : 1.0f;
-                    float dps = 0.0f;   // this lane's share of dp over the wave's 32 columns
+                    } else {
+                        const float pr = (probs && rv) ? probs[grow] : 1.0f;
+                        float dps = 0.0f;   // this lane's share of dp over the wave's 32 columns
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int f = it.col0 + wave * 32 + 8 * g + 4 * (lane >> 5);
-                        if (rv && f < N) {
-                            const uint16_t* hp = p.aux + grow * (2 * N) + f;
-                            const uint2 hg = *reinterpret_cast<const uint2*>(hp);
-                            const uint2 hu = *reinterpret_cast<const uint2*>(hp + N);
+                        for (int g = 0; g < 4; ++g) {
+                            const int cl = wave * 32 + 8 * g + 4 * (lane >> 5);
+                            const bool fv = rv && it.col0 + cl < N;
+                            uint16_t* sg = stg + r * SLD + cl;
+                            const uint2 hg = *reinterpret_cast<const uint2*>(sg);
+                            const uint2 hu = *reinterpret_cast<const uint2*>(sg + S_COLS);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
                             float dg[4], du[4];
@@ -714,20 +746,45 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 const float dap = probs ? pr * da : da;
                                 dg[x] = dap * uu * sgm * (1.0f + slope * gg * (1.0f - sgm));
                                 du[x] = dap * gg * sgm;
-                                dps += da * (gg * sgm * uu);
+                                if (fv) dps += da * (gg * sgm * uu);
                             }
-                            uint16_t* dh = p.out0 + grow * (2 * N) + f;
-                            *reinterpret_cast<uint2*>(dh) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
-                            *reinterpret_cast<uint2*>(dh + N) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+                            *reinterpret_cast<uint2*>(sg) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+                            *reinterpret_cast<uint2*>(sg + S_COLS) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+                        }
+                        if (dp_part) {
+                            // lanes l and l + 32 hold the two halves of the row's 32 columns
+                            const float tot = dps + __shfl_xor(dps, 32, 64);
+                            const int c0 = it.col0 + wave * 32;
+                            if (lane < 32 && rv && c0 < N) dp_part[grow * p.dp_ld + c0 / 32] = tot;
                         }
                     }
-                    if (dp_part) {
-                        // lanes l and l + 32 hold the two halves of the row's 32 columns
-                        const float tot = dps + __shfl_xor(dps, 32, 64);
-                        const int c0 = it.col0 + wave * 32;
-                        if (lane < 32 && rv && c0 < N) dp_part[grow * p.dp_ld + c0 / 32] = tot;
+                }
+                block_barrier();
+                if (cwave) {
+                    for (int idx = wave * 64 + lane; idx < 32 * SCH; idx += S_WAVES * 64) {
+                        const int sr = idx / SCH, sc = idx % SCH;
+                        const int row = b * 32 + sr;
+                        const uint4 v = *reinterpret_cast<const uint4*>(stg + sr * SLD + sc * 8);
+                        if (row < it.rows) {
+                            const int64_t orow = it.row0 + row;
+                            if constexpr (EPI == EPI_STORE) {
+                                const int col = it.col0 + sc * 8;
+                                if (col < N) *reinterpret_cast<uint4*>(p.out0 + orow * N + col) = v;
+                            } else if constexpr (EPI == EPI_SWIGLU) {
+                                const int arr = sc / (SCH / 3), f = it.col0 + (sc % (SCH / 3)) * 8;
+                                if (f < N) {
+                                    if (arr == 0) *reinterpret_cast<uint4*>(p.out0 + orow * N + f) = v;
+                                    else if (p.out1)
+                                        *reinterpret_cast<uint4*>(p.out1 + orow * (2 * N) + (arr - 1) * N + f) = v;
+                                }
+                            } else {
+                                const int arr = sc / (SCH / 2), f = it.col0 + (sc % (SCH / 2)) * 8;
+                                if (f < N) *reinterpret_cast<uint4*>(p.out0 + orow * (2 * N) + arr * N + f) = v;
+                            }
+                        }
                     }
                 }
+                if (b + 1 < nblk) block_barrier();   // the next block overwrites the array
             }
         };
 
@@ -760,16 +817,16 @@ void grouped_gemm_kernel(const GemmParams p) {
             block_barrier();
             const int nblk = (it_c.rows + 31) / 32;
             if (s_mma_wave) s_mma(q % S_NST, kt, nblk);
-            if (kt == kiters - 1) {
-                if (s_mma_wave) s_epilogue(it_c, nblk);
-                szero();
-                if (q + 1 < nq) it_c = item_of(q / kiters + 1);
-            }
             // every wave has read stage q-1 (the barrier above waited for the
             // reads): the copy waves refill its slot
             if (q + S_NST - 1 < nq) {
                 issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
                 advance();
+            }
+            if (kt == kiters - 1) {
+                s_epilogue(it_c, nblk, q % S_NST);
+                szero();
+                if (q + 1 < nq) it_c = item_of(q / kiters + 1);
             }
         }
         // the tile loop reuses the LDS
