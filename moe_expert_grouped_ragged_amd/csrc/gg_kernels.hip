@@ -605,48 +605,59 @@ void grouped_gemm_kernel(const GemmParams p) {
         // K positions >= K (last stage only) are zeroed in the fragments, so
         // whatever the copies left there adds nothing (the tile flavor adds the
         // same zero products).  Every fragment read of the stage is issued
-        // before its MFMAs, so the LDS latency is paid once per stage.
+        // before its MFMAs, in two k32 halves (which bounds the fragment
+        // registers), so the LDS latency is paid twice per stage; the token
+        // fragments of all S_BLK blocks are read whatever nblk is (the panel
+        // always holds SMALL_M rows), which keeps the reads independent.
         auto s_mma = [&](int slot_i, int kt, int nblk) {
             const uint16_t* sw = s_buf + slot_i * S_EL;
             const uint16_t* sx = sw + SW_EL;
-            const bool last = k_tail && kt == kiters - 1;
-            constexpr int NJ = BK / 16;
-            bf16x8 wf[NJ], xf[NJ][S_BLK];
+            constexpr int NJ = BK / 16, NH = NJ / 2;
+            const bool last = k_tail && kt == kiters - 1;   // uniform: only the last stage has a tail
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int ch = 2 * j + (lane >> 5);
-                if constexpr (!W_KN) {
-                    wf[j] = *reinterpret_cast<const bf16x8*>(sw + kc_off(wave * 32 + (lane & 31), ch));
-                } else {
-                    const int g = lane >> 4;
-                    const int kb = j * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
-                    const int n = wave * 32 + 16 * (g & 1) + 4 * (lane & 3);
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb, n))));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb + 4, n))));
-                    wf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int h = 0; h < 2; ++h) {   // two k32 halves: bounds the fragment registers
+                bf16x8 wf[NH], xf[NH][S_BLK];
+#pragma unroll
+                for (int jj = 0; jj < NH; ++jj) {
+                    const int j = h * NH + jj;
+                    const int ch = 2 * j + (lane >> 5);
+                    if constexpr (!W_KN) {
+                        wf[jj] = *reinterpret_cast<const bf16x8*>(sw + kc_off(wave * 32 + (lane & 31), ch));
+                    } else {
+                        const int g = lane >> 4;
+                        const int kb = j * 16 + 8 * (g >> 1) + ((lane >> 2) & 3);
+                        const int n = wave * 32 + 16 * (g & 1) + 4 * (lane & 3);
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb, n))));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            reinterpret_cast<__attribute__((address_space(3))) i16x4*>(GG_AS3(sw + snc_off(kb + 4, n))));
+                        wf[jj] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+#pragma unroll
+                    for (int b = 0; b < S_BLK; ++b)
+                        xf[jj][b] = *reinterpret_cast<const bf16x8*>(sx + kc_off(b * 32 + (lane & 31), ch));
+                }
+                if (last) {
+#pragma unroll
+                    for (int jj = 0; jj < NH; ++jj) {
+                        if (kt * BK + (h * NH + jj) * 16 + 8 * (lane >> 5) >= K) {
+                            const bf16x8 z = {};
+                            wf[jj] = z;
+#pragma unroll
+                            for (int b = 0; b < S_BLK; ++b) xf[jj][b] = z;
+                        }
+                    }
                 }
 #pragma unroll
-                for (int b = 0; b < S_BLK; ++b)
-                    xf[j][b] = (b == 0 || b < nblk)
-                                   ? *reinterpret_cast<const bf16x8*>(sx + kc_off(b * 32 + (lane & 31), ch))
-                                   : xf[j][0];
-            }
+                for (int jj = 0; jj < NH; ++jj) {
+                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jj], xf[jj][0], sacc[0], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if (last && kt * BK + j * 16 + 8 * (lane >> 5) >= K) {
-                    const bf16x8 z = {};
-                    wf[j] = z;
-#pragma unroll
-                    for (int b = 0; b < S_BLK; ++b) xf[j][b] = z;
+                    for (int b = 1; b < S_BLK; ++b)
+                        if (b < nblk) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jj], xf[jj][b], sacc[b], 0, 0, 0);
                 }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j][0], sacc[0], 0, 0, 0);
-#pragma unroll
-                for (int b = 1; b < S_BLK; ++b)
-                    if (b < nblk) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j][b], sacc[b], 0, 0, 0);
             }
         };
+
         // Item epilogue, staged through the ring slot of the item's last stage:
         // every wave has finished reading it at the first barrier below, and
         // the copy waves refill it only after the next stage's barrier.  Per
@@ -701,8 +712,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                         for (int g = 0; g < 4; ++g) {
                             const int cl = wave * 32 + 8 * g + 4 * (lane >> 5);
                             *reinterpret_cast<uint2*>(stg + r * SLD + cl) =
-                                make_uint2(pack2(sacc[b][4 * g], sacc[b][4 * g + 1]),
-                                           pack2(sacc[b][4 * g + 2], sacc[b][4 * g + 3]));
+                                make_uint2(pack2(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
+                                           pack2(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3])));
                         }
                     } else if constexpr (EPI == EPI_SWIGLU) {
                         const float pr = (probs && rv) ? probs[grow] : 1.0f;
@@ -712,8 +723,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                             uint32_t gb[4], ub[4], ab[4];
 #pragma unroll
                             for (int x = 0; x < 4; ++x) {
-                                gb[x] = f2bf(sacc[b][4 * g + x]);
-                                ub[x] = f2bf(sacc[b][4 * g + 8 + x]);
+                                gb[x] = f2bf(acc_rd(sacc[b][4 * g + x]));
+                                ub[x] = f2bf(acc_rd(sacc[b][4 * g + 8 + x]));
                                 const float gg = bf2f(gb[x]);
                                 const float uu = bf2f(ub[x]);
                                 const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
@@ -741,7 +752,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                             for (int x = 0; x < 4; ++x) {
                                 const float gg = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
                                 const float uu = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
-                                const float da = bf2f(f2bf(sacc[b][4 * g + x]));
+                                const float da = bf2f(f2bf(acc_rd(sacc[b][4 * g + x])));
                                 const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg)));
                                 const float dap = probs ? pr * da : da;
                                 dg[x] = dap * uu * sgm * (1.0f + slope * gg * (1.0f - sgm));
