@@ -799,7 +799,6 @@ void grouped_gemm_kernel(const GemmParams p) {
             }
         };
 
-        szero();
         SItem it_d = item_of(0);   // copy cursor
         int d_i = 0, d_kt = 0;
         auto advance = [&]() {
@@ -813,32 +812,38 @@ void grouped_gemm_kernel(const GemmParams p) {
                 issue_s(it_d, d_kt, q);
                 advance();
             }
-        SItem it_c = item_of(0);   // compute cursor
-        const bool s_mma_wave = wave < S_WAVES;
-        for (int q = 0; q < nq; ++q) {
-            const int kt = q % kiters;
-            // the copy waves wait for stage q (up to S_NST - 2 later stages stay
-            // in flight); the barrier publishes it to the compute waves
-            const int newer = min(S_NST - 2, nq - 1 - q);
-            if (!s_mma_wave) {
-                if (newer >= 2) wait_vmcnt<2 * LPS_S>();
-                else if (newer == 1) wait_vmcnt<LPS_S>();
-                else wait_vmcnt<0>();
-            }
-            block_barrier();
+        // One pass per item, with the K stages inside.  Compute waves and copy
+        // waves run separate copies of the stage loop with the same barrier
+        // sequence (one per stage), so that only MFMA results cross the compute
+        // loop's back edge and the accumulators stay in AGPRs.
+        for (int i = 0, q = 0; i < n_my; ++i, q += kiters) {
+            const SItem it_c = item_of(i);   // compute cursor
             const int nblk = (it_c.rows + 31) / 32;
-            if (s_mma_wave) s_mma(q % S_NST, kt, nblk);
-            // every wave has read stage q-1 (the barrier above waited for the
-            // reads): the copy waves refill its slot
-            if (q + S_NST - 1 < nq) {
-                issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
-                advance();
-            }
-            if (kt == kiters - 1) {
-                s_epilogue(it_c, nblk, q % S_NST);
+            if (wave < S_WAVES) {
                 szero();
-                if (q + 1 < nq) it_c = item_of(q / kiters + 1);
+                for (int kt = 0; kt < kiters; ++kt) {
+                    block_barrier();   // stage q + kt has landed
+                    s_mma((q + kt) % S_NST, kt, nblk);
+                }
+            } else {
+                for (int kt = 0; kt < kiters; ++kt) {
+                    const int qq = q + kt;
+                    // wait for stage qq (up to S_NST - 2 later stages stay in flight);
+                    // the barrier publishes it to the compute waves
+                    const int newer = min(S_NST - 2, nq - 1 - qq);
+                    if (newer >= 2) wait_vmcnt<2 * LPS_S>();
+                    else if (newer == 1) wait_vmcnt<LPS_S>();
+                    else wait_vmcnt<0>();
+                    block_barrier();
+                    // every wave has read stage qq-1 (the barrier waited for the
+                    // reads): refill its slot
+                    if (qq + S_NST - 1 < nq) {
+                        issue_s(it_d, d_kt, (qq + S_NST - 1) % S_NST);
+                        advance();
+                    }
+                }
             }
+            s_epilogue(it_c, nblk, (q + kiters - 1) % S_NST);
         }
         // the tile loop reuses the LDS
         block_barrier();
