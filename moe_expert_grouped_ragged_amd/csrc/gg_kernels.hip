@@ -282,14 +282,13 @@ void grouped_gemm_kernel(const GemmParams p) {
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int tiles_n = (N + TILE_COLS - 1) / TILE_COLS;
     // streaming flavor: an item is the streamed rows of one expert x S_COLS output
-    // columns (256 weight rows: for SwiGLU 128 gate rows and the matching 128 up rows)
+    // columns (192 weight rows: for SwiGLU 96 gate rows and the matching 96 up rows)
     constexpr int S_ROWS = 192;                                   // weight rows per item
     constexpr int S_COLS = (EPI == EPI_SWIGLU) ? S_ROWS / 2 : S_ROWS;
     const int items_n = (N + S_COLS - 1) / S_COLS;
     static_assert(TBM == 256, "tile_rows_of assumes 256-row tiles");
     build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, s_off, s_pre, s_spre);
-    const int n_stream = uni(s_spre[E]);
-    const int total = n_stream + uni(s_pre[E]);
+    const int n_items = uni(s_spre[E]);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -306,6 +305,12 @@ void grouped_gemm_kernel(const GemmParams p) {
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int slot = (G % 8 == 0) ? (b & 7) * (G >> 3) + (b >> 3) : b;
+    // When the streaming items fit into the grid twice over, each is split into
+    // two halves of S_ROWS / 2 weight rows (three compute waves), so that no
+    // workgroup takes a whole item while others take none.  A row's arithmetic
+    // is the same either way.
+    const int s_sh = (2 * n_items <= G) ? 1 : 0;   // log2 of the halves per item
+    const int n_stream = n_items << s_sh;
 
     // ---- per-tile state (wave-uniform values live in SGPRs)
     int row0 = 0, row_end = 0, col0 = 0;
@@ -543,18 +548,20 @@ void grouped_gemm_kernel(const GemmParams p) {
     auto snc_off = [](int k, int n) { return k * S_ROWS + (((n >> 3) ^ ((k & 3) << 1)) << 3) + (n & 7); };
     static_assert(S_NST * S_EL <= LDS_BUF_EL, "streaming stages fit in LDS");
     struct SItem { int e, row0, rows, col0; };
+    const int s_aw = S_WAVES >> s_sh;            // compute waves with rows in an item
     auto stream_items = [&](int t0) -> int {
         const int n_my = (n_stream - t0 + G - 1) / G;
         const int nq = n_my * kiters;
         const uint32_t s_lds0 = lds_addr(s_buf);
         auto item_of = [&](int i) -> SItem {
             const int t = t0 + i * G;
+            const int tf = t >> s_sh;                // whole item
             SItem it;
-            it.e = uni(find_expert(s_spre, E, t));
+            it.e = uni(find_expert(s_spre, E, tf));
             const int rb = uni(s_off[it.e]), re = uni(s_off[it.e + 1]);
             it.row0 = rb + tile_rows_of(re - rb);   // the rows the tiles leave
             it.rows = re - it.row0;
-            it.col0 = (t - uni(s_spre[it.e])) * S_COLS;
+            it.col0 = (tf - uni(s_spre[it.e])) * S_COLS + (t & s_sh) * (S_COLS / 2);
             return it;
         };
         auto issue_s = [&](const SItem& it, int kt, int slot_i) {
@@ -567,21 +574,25 @@ void grouped_gemm_kernel(const GemmParams p) {
             for (int i = 0; i < SW_PW; ++i) {
                 const int pos = (cw * SW_PW + i) * 64 + lane;
                 uint32_t voff;
+                // a half item's unused panel half re-reads its used half (L2
+                // hits), so every stage issues the same number of copies
                 if constexpr (!W_KN) {
                     const int r = pos >> 3;
                     const int c = (pos & 7) ^ kswz(r);
+                    const int rr = (s_sh && r >= S_ROWS / 2) ? r - S_ROWS / 2 : r;
                     int wrow;
                     if constexpr (EPI == EPI_SWIGLU) {
-                        const int q = r & 31;
-                        wrow = min(it.col0 + (r >> 5) * 16 + (q & 15), N - 1) + (q >= 16 ? p.up_off : 0);
+                        const int q = rr & 31;
+                        wrow = min(it.col0 + (rr >> 5) * 16 + (q & 15), N - 1) + (q >= 16 ? p.up_off : 0);
                     } else {
-                        wrow = min(it.col0 + r, N - 1);
+                        wrow = min(it.col0 + rr, N - 1);
                     }
                     voff = static_cast<uint32_t>((wrow * p.ldw + min(k0 + c * 8, K - 8)) * 2);
                 } else {
                     const int kr = pos / S_CPR;
                     const int c = (pos % S_CPR) ^ ((kr & 3) << 1);
-                    voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + c * 8, N - 8)) * 2);
+                    const int cc = (s_sh && c >= S_CPR / 2) ? c - S_CPR / 2 : c;
+                    voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + cc * 8, N - 8)) * 2);
                 }
                 dma16(wb, voff, base + (cw * SW_PW + i) * 1024);
             }
@@ -676,9 +687,11 @@ void grouped_gemm_kernel(const GemmParams p) {
         static_assert(SC % 8 == 0 && S_STG_DMA * 1024 <= S_EL * 2, "staging fits in a ring slot");
         auto s_epilogue = [&](const SItem& it, int nblk, int slot_i) {
             uint16_t* stg = s_buf + slot_i * S_EL;
-            const bool cwave = wave < S_WAVES;
+            const bool cwave = wave < S_WAVES;  // stores
+            const bool awave = wave < s_aw;     // holds results of this item
+            const int col_end = min(N, it.col0 + (S_COLS >> s_sh));
             block_barrier();                    // every wave is done with the slot
-            if (cwave) mfma_drain();
+            if (awave) mfma_drain();
 #pragma unroll
             for (int b = 0; b < S_BLK; ++b) {
                 if (b >= nblk) break;           // nblk is uniform over the workgroup
@@ -706,7 +719,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                     }
                     block_barrier();
                 }
-                if (cwave) {
+                if (awave) {
                     if constexpr (EPI == EPI_STORE) {
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
@@ -780,17 +793,17 @@ void grouped_gemm_kernel(const GemmParams p) {
                             const int64_t orow = it.row0 + row;
                             if constexpr (EPI == EPI_STORE) {
                                 const int col = it.col0 + sc * 8;
-                                if (col < N) *reinterpret_cast<uint4*>(p.out0 + orow * N + col) = v;
+                                if (col < col_end) *reinterpret_cast<uint4*>(p.out0 + orow * N + col) = v;
                             } else if constexpr (EPI == EPI_SWIGLU) {
                                 const int arr = sc / (SCH / 3), f = it.col0 + (sc % (SCH / 3)) * 8;
-                                if (f < N) {
+                                if (f < col_end) {
                                     if (arr == 0) *reinterpret_cast<uint4*>(p.out0 + orow * N + f) = v;
                                     else if (p.out1)
                                         *reinterpret_cast<uint4*>(p.out1 + orow * (2 * N) + (arr - 1) * N + f) = v;
                                 }
                             } else {
                                 const int arr = sc / (SCH / 2), f = it.col0 + (sc % (SCH / 2)) * 8;
-                                if (f < N) *reinterpret_cast<uint4*>(p.out0 + orow * (2 * N) + arr * N + f) = v;
+                                if (f < col_end) *reinterpret_cast<uint4*>(p.out0 + orow * (2 * N) + arr * N + f) = v;
                             }
                         }
                     }
@@ -813,37 +826,46 @@ void grouped_gemm_kernel(const GemmParams p) {
                 advance();
             }
         // One pass per item, with the K stages inside.  Compute waves and copy
-        // waves run separate copies of the stage loop with the same barrier
-        // sequence (one per stage), so that only MFMA results cross the compute
-        // loop's back edge and the accumulators stay in AGPRs.
-        for (int i = 0, q = 0; i < n_my; ++i, q += kiters) {
-            const SItem it_c = item_of(i);   // compute cursor
-            const int nblk = (it_c.rows + 31) / 32;
-            if (wave < S_WAVES) {
-                szero();
-                for (int kt = 0; kt < kiters; ++kt) {
-                    block_barrier();   // stage q + kt has landed
-                    s_mma((q + kt) % S_NST, kt, nblk);
+        // waves run separate copies of the item loop with the same barrier
+        // sequence (one per stage, then the epilogue's), so that only MFMA
+        // results cross the compute loop's back edge (the accumulators stay in
+        // AGPRs) and neither role keeps the other's state live.
+        if (wave < S_WAVES) {
+            for (int i = 0, q = 0; i < n_my; ++i, q += kiters) {
+                const SItem it_c = item_of(i);
+                const int nblk = (it_c.rows + 31) / 32;
+                if (wave < s_aw) {
+                    szero();
+                    for (int kt = 0; kt < kiters; ++kt) {
+                        block_barrier();   // stage q + kt has landed
+                        s_mma((q + kt) % S_NST, kt, nblk);
+                    }
+                } else {   // no rows in a half item
+                    for (int kt = 0; kt < kiters; ++kt) block_barrier();
                 }
-            } else {
-                for (int kt = 0; kt < kiters; ++kt) {
-                    const int qq = q + kt;
-                    // wait for stage qq (up to S_NST - 2 later stages stay in flight);
+                s_epilogue(it_c, nblk, (q + kiters - 1) % S_NST);
+            }
+        } else {
+            for (int i = 0, q = 0; i < n_my; ++i) {
+                for (int kt = 0; kt < kiters; ++kt, ++q) {
+                    // wait for stage q (up to S_NST - 2 later stages stay in flight);
                     // the barrier publishes it to the compute waves
-                    const int newer = min(S_NST - 2, nq - 1 - qq);
+                    const int newer = min(S_NST - 2, nq - 1 - q);
                     if (newer >= 2) wait_vmcnt<2 * LPS_S>();
                     else if (newer == 1) wait_vmcnt<LPS_S>();
                     else wait_vmcnt<0>();
                     block_barrier();
-                    // every wave has read stage qq-1 (the barrier waited for the
+                    // every wave has read stage q-1 (the barrier waited for the
                     // reads): refill its slot
-                    if (qq + S_NST - 1 < nq) {
-                        issue_s(it_d, d_kt, (qq + S_NST - 1) % S_NST);
+                    if (q + S_NST - 1 < nq) {
+                        issue_s(it_d, d_kt, (q + S_NST - 1) % S_NST);
                         advance();
                     }
                 }
+                // the epilogue's barriers (its work belongs to the compute waves)
+                const SItem it_e = item_of(i);
+                s_epilogue(it_e, (it_e.rows + 31) / 32, (q - 1) % S_NST);
             }
-            s_epilogue(it_c, nblk, (q + kiters - 1) % S_NST);
         }
         // the tile loop reuses the LDS
         block_barrier();
@@ -853,8 +875,9 @@ void grouped_gemm_kernel(const GemmParams p) {
     // ---- streaming flavor first (work items [0, n_stream)), then the tiles
     int t = slot;
     if (t < n_stream) t = uni(stream_items(t));
-    for (; t < total; t += G) {
-        setup_tile(t - n_stream);
+    const int n_tiles = uni(s_pre[E]);
+    for (int tt = t - n_stream; tt < n_tiles; tt += G) {
+        setup_tile(tt);
 #pragma unroll
         for (int s = 0; s < NSTAGE; ++s)
             if (s < kiters) issue(s);
