@@ -4,7 +4,10 @@ One set of token rows routed to one expert's weights is computed inside many
 different batches: alone (a small expert, weight-streaming flavor), as the
 head of a large expert (256-row tiles), as the streamed tail of a large
 expert, shifted by row counts that are not multiples of 32 (so the rows land
-in other MFMA lanes), in another expert slot, and beside other experts.  Both
+in other MFMA lanes), in another expert slot, and beside other experts.  As
+the streamed tail of a 2048-row expert the grid is large next to the number
+of streaming items, so each item is split into two halves of 96 weight rows;
+alone, the items stay whole.  Both
 flavors accumulate the same MFMA k-steps in the same order into fp32
 accumulators that start at zero, and share the epilogue arithmetic, so H1, A,
 Y, dH1 and dX of those rows must be bitwise equal in every batch.  The same holds for the weighted QuickGeGLU path, dprobs
@@ -33,6 +36,7 @@ def _layouts(R):
         "shifted_tail": [[("o", 259), ("R", R)]],
         "other_slot": [[("o", 100)], [], [("o", 3), ("R", R)], [("o", 70)]],
         "beside_others": [[("R", R)], [("o", 300)], [("o", 256)], [("o", 70)]],
+        "tail_of_wide": [[("o", 2048), ("R", R)]],
     }
 
 
@@ -88,7 +92,7 @@ def _run(layout, R, base, weighted=False):
 def test_rows_are_batch_invariant(H, F, R, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    base = workload.custom_case([R, 700], H, F, seed=31)
+    base = workload.custom_case([R, 2400], H, F, seed=31)
     ref = None
     for name, layout in _layouts(R).items():
         log(f"[invariance] H={H} F={F} R={R} {name}")
