@@ -9,7 +9,10 @@
 //
 // Two flavors share one launch.  Rows that fill 256-row tiles run as 256 x 256
 // output tiles; the at most 96 rows an expert leaves over (all rows of a
-// small expert) run as weight-streaming items, before the tiles.
+// small expert) run as weight-streaming items, before the tiles.  An item is
+// those rows x 192 weight rows (six compute waves of 32 rows; two more waves
+// issue every copy into a 4-stage ring), or x 96 weight rows when the items
+// fit into the grid twice over, so that they spread over all workgroups.
 //
 // Tile core: bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulators), 8 waves
 // of 128 token rows x 64 output columns.  Both operand panels stream from HBM
