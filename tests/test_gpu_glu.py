@@ -20,6 +20,7 @@ CASES = [
     ([31, 32, 63, 64, 65, 0, 1], 136, 200),
     ([300, 0, 257, 40, 1], 128, 96),
     ([0, 520, 0], 72, 264),
+    ([96, 95, 352, 0], 136, 200),   # three full 32-row blocks in streaming items
 ]
 
 

@@ -17,7 +17,8 @@ from parity import check_chained, check
 
 pytestmark = pytest.mark.gpu
 
-CASES = [([5, 0, 7, 33], 64, 64), ([31, 32, 63, 64, 65, 0, 1], 136, 200), ([300, 0, 257, 40, 1], 128, 96)]
+CASES = [([5, 0, 7, 33], 64, 64), ([31, 32, 63, 64, 65, 0, 1], 136, 200), ([300, 0, 257, 40, 1], 128, 96),
+         ([96, 95, 352, 0], 136, 200)]
 MODES = [("swiglu", False), ("qgeglu", True)]
 
 
