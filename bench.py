@@ -127,7 +127,7 @@ def launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args):
     import torch
     E, H, F = case.E, case.H, case.F
     off_h = case.offsets
-    per = 3 * F * H
+    per = gg.packed_bytes(1, H, F) // 2     # elements of one expert block
     live = [e for e in range(E) if off_h[e + 1] > off_h[e]]
     one = {e: torch.tensor([0, int(off_h[e + 1] - off_h[e])], dtype=torch.int64, device=x.device) for e in live}
 

@@ -75,7 +75,12 @@ typedef enum {
 /* Human-readable name of a status code (static string). */
 const char* gg_status_string(int status);
 
-/* Bytes of the packed weight buffer: 6*E*H*F (bf16 W1 and W2 of every expert). */
+/* Bytes of the packed weight buffer.  Expert-major blocks: expert e's block
+ * holds W1_e [2F][H] then W2_e [H][F], bf16 row-major.  When H % 256 == 0 and
+ * F % 128 == 0 the block also holds, after them, copies of W1_e and W2_e in
+ * MFMA fragment order (read by the forward tiles; written by gg_pack_weights):
+ * 12*E*H*F bytes in all, 6*E*H*F otherwise.  One expert block is itself a
+ * packed buffer with E = 1. */
 size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F);
 
 /* Bytes of the gg_dgrad workspace: dH1 [M][2F] bf16 = 4*M*F. */
@@ -87,7 +92,10 @@ size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F);
  * re-packing after one expert's weights were replaced copies only what
  * moved (recovery after a middle expert weight is replaced, "Why existing
  * behavior remains safe").  A source that partially overlaps `packed` gives
- * GG_ERR_ALIASING.  Copies are asynchronous device-to-device on `stream`. */
+ * GG_ERR_ALIASING.  Copies are asynchronous device-to-device on `stream`.
+ * The fragment-ordered copies (see gg_packed_bytes) are always rewritten, so
+ * after writing weights straight into the packed buffer, call this again
+ * with those locations as sources. */
 int gg_pack_weights(int64_t E, int64_t H, int64_t F,
                     const void* const* w1, const void* const* w2,
                     void* packed, size_t packed_bytes, hipStream_t stream);

@@ -134,7 +134,7 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Pack frozen expert weights (w1[e]: [2F, H], gate rows then up rows;
     w2[e]: [H, F]) into one expert-major bf16 buffer.  Returns the packed
-    buffer (1-D, 3*E*F*H elements).  Per-expert views into it:
+    buffer (1-D, packed_bytes(E, H, F) / 2 elements).  Per-expert views into it:
     ``expert_views(packed, E, H, F)``."""
     w1s = list(w1.unbind(0)) if isinstance(w1, torch.Tensor) else list(w1)
     w2s = list(w2.unbind(0)) if isinstance(w2, torch.Tensor) else list(w2)
@@ -164,8 +164,10 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
 
 
 def expert_views(packed: torch.Tensor, E: int, H: int, F: int):
-    """(w1_views, w2_views): per-expert views into the packed buffer."""
-    per = 3 * F * H
+    """(w1_views, w2_views): per-expert views into the packed buffer.  After
+    writing through them, call gg_pack_weights(w1_views, w2_views, packed=packed)
+    so that the derived fragment-ordered copies follow."""
+    per = packed_bytes(1, H, F) // 2
     w1 = [packed[e * per:e * per + 2 * F * H].view(2 * F, H) for e in range(E)]
     w2 = [packed[e * per + 2 * F * H:(e + 1) * per].view(H, F) for e in range(E)]
     return w1, w2

@@ -111,13 +111,19 @@ int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStre
     return GG_OK;
 }
 
+// Shapes whose packed buffer also holds the fragment-ordered copies read by
+// the four-wave forward tiles.
+bool has_frag(int64_t H, int64_t F) { return H % 256 == 0 && F % 128 == 0; }
+// Elements of one expert block of the packed buffer.
+int64_t expert_block(int64_t H, int64_t F) { return (has_frag(H, F) ? 6 : 3) * F * H; }
+
 gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed, int64_t E,
                            int64_t H, int64_t F) {
     gg::GemmParams p{};
     p.offsets = offsets;
     p.M = static_cast<int>(M);
     p.E = static_cast<int>(E);
-    p.w_expert_stride = 3 * F * H;
+    p.w_expert_stride = expert_block(H, F);
     p.w = static_cast<const uint16_t*>(packed);
     p.up_off = static_cast<int>(F);
     p.slope = 1.0f;
@@ -156,8 +162,7 @@ const char* gg_status_string(int status) {
 
 size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F) {
     if (E <= 0 || H <= 0 || F <= 0) return 0;
-    return static_cast<size_t>(6) * static_cast<size_t>(E) * static_cast<size_t>(H) *
-           static_cast<size_t>(F);
+    return static_cast<size_t>(2) * static_cast<size_t>(E) * static_cast<size_t>(expert_block(H, F));
 }
 
 size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F) {
@@ -182,7 +187,7 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, cons
     if (packed_bytes < need) return GG_ERR_WORKSPACE_TOO_SMALL;
     const size_t w1_bytes = static_cast<size_t>(2 * F * H) * 2;
     const size_t w2_bytes = static_cast<size_t>(H * F) * 2;
-    const size_t per_expert = w1_bytes + w2_bytes;
+    const size_t per_expert = static_cast<size_t>(expert_block(H, F)) * 2;
     const Range whole = range_of(packed, need);
     char* base = static_cast<char*>(packed);
     for (int64_t e = 0; e < E; ++e) {
@@ -207,6 +212,10 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, cons
             hipMemcpyAsync(d2, w2[e], w2_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return GG_ERR_HIP;
     }
+    if (has_frag(H, F) &&
+        gg::launch_pack_frag(static_cast<uint16_t*>(packed), static_cast<int>(E), static_cast<int>(H),
+                             static_cast<int>(F), stream) != hipSuccess)
+        return GG_ERR_HIP;
     return GG_OK;
 }
 
@@ -246,6 +255,7 @@ int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const v
     p.out1 = static_cast<uint16_t*>(h1_out);
     p.slope = slope;
     p.probs = probs;
+    if (has_frag(H, F)) p.wfrag = static_cast<const uint16_t*>(packed) + 3 * F * H;
     return gg::launch_fc1_swiglu(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
@@ -271,6 +281,7 @@ int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void*
     p.N = static_cast<int>(H);
     p.ldw = static_cast<int>(F);
     p.out0 = static_cast<uint16_t*>(y);
+    if (has_frag(H, F)) p.wfrag = static_cast<const uint16_t*>(packed) + 5 * F * H;
     return gg::launch_fc2(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 

@@ -32,12 +32,18 @@ struct GemmParams {
     float* dp_part;            // derivative variant: partial sums of dp per row and
                                // 32-column group [M][dp_ld], or null
     int dp_ld;                 // ceil(N / 32)
+    // Forward GEMMs: this GEMM's matrix in the fragment-ordered copy (same
+    // expert stride), or null.  With it, the tiles run in a four-wave launch.
+    const uint16_t* wfrag;
+    int stream_only;           // run only the streaming items (tiles launched separately)
 };
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
+// Fragment-ordered copies of W1 and W2 inside every expert block (H % 256 == 0, F % 128 == 0).
+hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 // dprobs[r] = sum over g of part[r][g] in increasing g, for the routed rows.
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,

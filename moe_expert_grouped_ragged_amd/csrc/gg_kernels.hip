@@ -878,7 +878,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     // ---- streaming flavor first (work items [0, n_stream)), then the tiles
     int t = slot;
     if (t < n_stream) t = uni(stream_items(t));
-    const int n_tiles = uni(s_pre[E]);
+    const int n_tiles = p.stream_only ? 0 : uni(s_pre[E]);   // tiles of a separate launch
     for (int tt = t - n_stream; tt < n_tiles; tt += G) {
         setup_tile(tt);
 #pragma unroll
@@ -1179,6 +1179,287 @@ void grouped_gemm_kernel(const GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------- four-wave tiles
+//
+// Forward tiles over a fragment-ordered copy of the weights (present in the
+// packed buffer when H % 256 == 0 and F % 128 == 0).  Four waves compute a
+// 256 x 256 tile: wave w owns token rows (w >> 1) * 128 .. +127 and weight rows
+// (w & 1) * 128 .. +127, as 4 x 4 accumulator blocks of 32 x 32 (all 256
+// AGPRs).  Tokens stream through a 4-slot LDS ring of 64-k stages by LDS-DMA,
+// three stages ahead.  Weights skip LDS: in the fragment-ordered copy the 64
+// lanes' 16-byte operands of one 32-row x 16-k block lie next to each other,
+// so every lane loads its own MFMA operand straight into VGPRs with one
+// coalesced 1 KiB load per block, seven k16 steps ahead into an 8-step
+// register ring.  Every k16 step issues the same six loads (its four weight
+// blocks seven steps ahead and two of the eight token copies of the stage
+// three stages ahead), so the number of loads issued after any one of them
+// is fixed and the waits are constant counts: a step's weights are complete
+// at vmcnt(38), a stage's token copies at vmcnt(48).  Virtual steps -12..-1
+// repeat the pattern as the prologue, and the steps past the end re-load
+// clamped addresses, so the counts hold everywhere.  The sums are the same
+// MFMA chain over k as in the eight-wave tiles and the streaming items, so a
+// row's results do not depend on which flavor computed it.
+//
+// Fragment order: block b of 32 weight rows and k16 step s of an expert is
+// 512 contiguous elements; lane l's 8 are rows 32b + (l & 31), k 16s + 8(l >> 5).
+// For W1 the 32-row blocks go gate, gate, up, up per 64 features, so a wave's
+// four blocks are the gate and up rows of the same 64 features.
+constexpr int T4_THREADS = 256;
+constexpr int T4_SLOT = 256 * BK;          // elements of one token stage
+constexpr int T4_NSLOT = 4;
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Load one 16-byte weight fragment.  The register is an in/out operand so
+// that a load's destination stays reserved until the next load into the same
+// ring slot (also for the loads whose data is never used).
+__device__ __forceinline__ void wfrag_load(bf16x8& w, const uint16_t* ptr) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(w) : "v"(ptr) : "memory");
+}
+#pragma clang diagnostic pop
+// Wait for the weight fragments of the current step: at most 38 loads issued
+// after them may be outstanding.  The registers are tied to the wait so that
+// nothing reads them before it.
+__device__ __forceinline__ void wfrag_wait38(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
+    asm volatile("s_waitcnt vmcnt(38)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
+}
+__device__ __forceinline__ void wfrag_hold(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
+}
+
+template <int EPI, bool EXT>
+__global__ __launch_bounds__(T4_THREADS, 1)
+void tile4_kernel(const GemmParams p) {
+    static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues only");
+    const float slope = EXT ? p.slope : 1.0f;
+    const float* const probs = EXT ? p.probs : nullptr;
+    __shared__ __attribute__((aligned(1024))) uint16_t s_ring[T4_NSLOT * T4_SLOT];
+    __shared__ int s_off[GG_KMAX_EXPERTS + 1];
+    __shared__ int s_pre[GG_KMAX_EXPERTS + 1];
+    __shared__ int s_spre[GG_KMAX_EXPERTS + 1];
+    const int E = p.E, M = p.M, K = p.K, N = p.N;
+    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
+    constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 96 : 192;     // streaming items (counted, not run here)
+    const int tiles_n = N / TILE_COLS;
+    build_schedule<T4_THREADS>(p.offsets, E, M, tiles_n, (N + S_COLS - 1) / S_COLS, s_off, s_pre, s_spre);
+    const int n_tiles = uni(s_pre[E]);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uni(tid >> 6);
+    const int wg = wave >> 1;            // token rows wg*128 .. +127
+    const int wn = wave & 1;             // weight rows wn*128 .. +127 of the tile
+    const int kiters = K / BK, nsteps = K / 16;
+    const int G = gridDim.x, b = blockIdx.x;
+    const int slot = (G % 8 == 0) ? (b & 7) * (G >> 3) + (b >> 3) : b;
+    const uint32_t ring_l = lds_addr(s_ring);
+    // LDS-DMA: lane tid moves chunk (tid & 7) of row (tid >> 3) + 32 i; the
+    // logical k chunk stored there follows the [row][64 k] swizzle.
+    const int lc = ((tid & 7) ^ kswz(tid >> 3)) * 8;
+
+    f32x16 acc[4][4];
+    bf16x8 wr[8][4];
+    bf16x8 tf[2][4];
+
+    for (int t = slot; t < n_tiles; t += G) {
+        const int e = uni(find_expert(s_pre, E, t));
+        const int local = t - uni(s_pre[e]);
+        const int rb = uni(s_off[e]);
+        const int row_end = uni(s_off[e + 1]);
+        const int tiles_m = tiles_m_of(row_end - rb);
+        const int row0 = uni(rb + (local % tiles_m) * TBM);
+        const int col0 = uni((local / tiles_m) * TILE_COLS);
+        const int rows = min(TBM, row_end - row0);
+        const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
+        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.w_expert_stride;
+        // first 32-row block of this wave in fragment order
+        const int rbw = (EPI == EPI_SWIGLU) ? (col0 / 64 + wn) * 4 : (col0 + wn * 128) / 32;
+        auto wptr = [&](int g, int j) -> const uint16_t* {
+            return wfe + ((static_cast<int64_t>(rbw + j) * nsteps + g) * 64 + lane) * 8;
+        };
+        // two of the eight LDS-DMA instructions of token stage s (clamped to the last)
+        auto tdma = [&](int s, int part) {
+            const int ss = s < kiters ? s : kiters - 1;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = 2 * part + u;
+                const int r = min((tid >> 3) + 32 * i, rows - 1);
+                const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * i) * 16;
+                dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
+            }
+        };
+        auto rd_t = [&](int g, int buf) {
+            const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
+            const int ch = 2 * (g & 3) + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(wg * 128 + i * 32 + (lane & 31), ch));
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        // prologue: virtual steps -12..-1 (weights of steps -5..6, token stages 0..2)
+#pragma unroll
+        for (int g = -12; g < 0; ++g) {
+            const int gw = g + 7;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wfrag_load(wr[(gw + 8) & 7][j], wptr(gw < 0 ? 0 : gw, j));
+            tdma((g >> 2) + 3, g & 3);
+        }
+        for (int g0 = 0; g0 < nsteps; g0 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int g = g0 + u;
+                const int j4 = u & 3;
+                if (j4 == 0) {
+                    wait_vmcnt<48>();    // this wave's copies of stage g / 4
+                    block_barrier();     // everyone's; slot (g / 4 - 1) % 4 is free again
+                    rd_t(g, u & 1);
+                }
+                if (j4 < 3) rd_t(g + 1, (u + 1) & 1);
+                wfrag_wait38(wr[u][0], wr[u][1], wr[u][2], wr[u][3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
+                const int gw = g + 7;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
+                tdma((g >> 2) + 3, j4);
+            }
+        }
+        // drain the clamped loads; the ring becomes the epilogue's staging area
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) wfrag_hold(wr[s][0], wr[s][1], wr[s][2], wr[s][3]);
+        block_barrier();
+        mfma_drain();
+        int opaque = 0;
+        asm volatile("" : "+s"(opaque));
+        const int wrow0 = row0 + wg * 128 + opaque;    // first token row of this wave
+        uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
+        if constexpr (EPI == EPI_STORE) {
+            // [128 rows][128 cols] bf16; 16-byte chunk c of row r at c ^ (r & 15)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = i * 32 + (lane & 31);
+                        const int c = j * 4 + q;
+                        uint2 v;
+                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                        *reinterpret_cast<uint2*>(stg + r * 128 + ((c ^ (r & 15)) << 3) + 4 * (lane >> 5)) = v;
+                    }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int gcol0 = col0 + wn * 128;
+#pragma unroll 4
+            for (int sidx = 0; sidx < 32; ++sidx) {
+                const int idx = sidx * 64 + lane;
+                const int r = idx >> 4, c = idx & 15;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + ((c ^ (r & 15)) << 3));
+                if (wrow0 + r < row_end)
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(wrow0 + r) * N + gcol0 + c * 8) = v;
+            }
+        } else {
+            // per pass of 64 token rows, [64][64] bf16 arrays for A, gate and up;
+            // 16-byte chunk c of row r at c ^ (r & 7)
+            uint16_t* sA = stg;
+            uint16_t* sG = stg + 4096;
+            uint16_t* sU = stg + 8192;
+            const int fcol0 = col0 + wn * 64;          // first feature of this wave
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = pass * 2 + ii;
+                    const int r = ii * 32 + (lane & 31);
+                    const int prow = wrow0 + pass * 64 + r;
+                    const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int c = jj * 4 + q;
+                            const int off = r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5);
+                            uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) {
+                                gb[x] = f2bf(acc_rd(acc[i][jj][q * 4 + x]));
+                                ub[x] = f2bf(acc_rd(acc[i][2 + jj][q * 4 + x]));
+                                const float gv = bf2f(gb[x]);
+                                const float uv = bf2f(ub[x]);
+                                const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
+                                const float v = sg * uv;
+                                ab[x] = f2bf(probs ? pr * v : v);
+                            }
+                            *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                            *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                            *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                        }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+                for (int sidx = 0; sidx < 8; ++sidx) {
+                    const int idx = sidx * 64 + lane;
+                    const int r = idx >> 3, c = idx & 7;
+                    const int off = r * 64 + ((c ^ (r & 7)) << 3);
+                    const int grow = wrow0 + pass * 64 + r;
+                    const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
+                    const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                    const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                    if (grow < row_end) {
+                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + fcol0 + c * 8) = va;
+                        if (p.out1) {
+                            uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + fcol0 + c * 8;
+                            *reinterpret_cast<uint4*>(h) = vg;
+                            *reinterpret_cast<uint4*>(h + N) = vu;
+                        }
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        }
+        block_barrier();   // staging reads done before the next tile's copies land
+    }
+}
+
+// Fragment-ordered copies of every expert's W1 and W2 (layout above), written
+// from the row-major matrices of the same expert block.
+__global__ void pack_frag_kernel(uint16_t* __restrict__ packed, int E, int H, int F) {
+    const int64_t stride_e = 6LL * H * F;                 // elements per expert block
+    const int64_t c1 = 2LL * F * H / 8, c2 = 1LL * H * F / 8;   // 16-byte chunks per matrix
+    const int64_t total = static_cast<int64_t>(E) * (c1 + c2);
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
+        const int e = static_cast<int>(i / (c1 + c2));
+        int64_t ci = i - static_cast<int64_t>(e) * (c1 + c2);
+        uint16_t* blk = packed + e * stride_e;
+        const bool second = ci >= c1;
+        if (second) ci -= c1;
+        const int K = second ? F : H;
+        const int l = static_cast<int>(ci & 63);
+        const int64_t rest = ci >> 6;
+        const int ks = static_cast<int>(rest % (K / 16));
+        const int rbk = static_cast<int>(rest / (K / 16));
+        int row;
+        if (second) {
+            row = rbk * 32 + (l & 31);
+        } else {
+            const int q = rbk & 3, fb = rbk >> 2;
+            row = (q < 2 ? 0 : F) + fb * 64 + (q & 1) * 32 + (l & 31);
+        }
+        const uint16_t* src = blk + (second ? 2LL * F * H : 0) + static_cast<int64_t>(row) * K + ks * 16 + (l >> 5) * 8;
+        uint16_t* dst = blk + (second ? 5LL * F * H : 3LL * F * H) + ci * 8;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    }
+}
+
 // Round n fp32 values to bf16 with the same conversion the epilogues use.
 __global__ void round_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -1221,12 +1502,47 @@ static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream
 
 static bool plain_swiglu(const GemmParams& p) { return p.slope == 1.0f && !p.probs && !p.dp_part; }
 
+template <int EPI, bool EXT>
+static hipError_t launch_tile4(const GemmParams& p, int num_cu, hipStream_t stream) {
+    constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
+    const int64_t tiles_n = p.N / TILE_COLS;
+    const int64_t tiles_m_max = (static_cast<int64_t>(p.M) + static_cast<int64_t>(p.E) * (TBM - 1)) / TBM;
+    int64_t grid = num_cu;
+    if (tiles_m_max * tiles_n < grid) grid = tiles_m_max * tiles_n;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((tile4_kernel<EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+// With a fragment-ordered weight copy (p.wfrag), the streaming items run as
+// one launch and the 256-row tiles as a second, four-wave launch.
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s) {
-    return plain_swiglu(p) ? launch_cfg<false, EPI_SWIGLU, false>(p, num_cu, s)
-                           : launch_cfg<false, EPI_SWIGLU, true>(p, num_cu, s);
+    const bool plain = plain_swiglu(p);
+    if (!p.wfrag)
+        return plain ? launch_cfg<false, EPI_SWIGLU, false>(p, num_cu, s)
+                     : launch_cfg<false, EPI_SWIGLU, true>(p, num_cu, s);
+    GemmParams q = p;
+    q.stream_only = 1;
+    hipError_t err = plain ? launch_cfg<false, EPI_SWIGLU, false>(q, num_cu, s)
+                           : launch_cfg<false, EPI_SWIGLU, true>(q, num_cu, s);
+    if (err != hipSuccess) return err;
+    return plain ? launch_tile4<EPI_SWIGLU, false>(p, num_cu, s) : launch_tile4<EPI_SWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
+    if (!p.wfrag) return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
+    GemmParams q = p;
+    q.stream_only = 1;
+    const hipError_t err = launch_cfg<false, EPI_STORE, false>(q, num_cu, s);
+    if (err != hipSuccess) return err;
+    return launch_tile4<EPI_STORE, false>(p, num_cu, s);
+}
+hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s) {
+    const int64_t chunks = static_cast<int64_t>(E) * 3 * H * F / 8;
+    int64_t blocks = (chunks + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_frag_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, packed, E, H, F);
+    return hipGetLastError();
 }
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     return plain_swiglu(p) ? launch_cfg<true, EPI_DSWIGLU, false>(p, num_cu, s)

@@ -21,6 +21,7 @@ CASES = [
     ([300, 0, 257, 40, 1], 128, 96),
     ([0, 520, 0], 72, 264),
     ([96, 95, 352, 0], 136, 200),   # three full 32-row blocks in streaming items
+    ([300, 0, 257, 40, 1, 97], 256, 128),   # four-wave forward tiles
 ]
 
 

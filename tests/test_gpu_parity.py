@@ -93,6 +93,10 @@ def test_tiny_workload():
     ([95, 96, 97, 0, 609], 64, 64),
     # the maximum expert count: mostly 0..5 rows, one large expert in the middle
     ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 64, 64),
+    # four-wave forward tiles (H % 256 == 0, F % 128 == 0): full and partial
+    # tiles, streamed tails on both sides of 96 rows, one- and two-iteration K loops
+    ([17, 0, 255, 256, 257, 600, 97, 96], 256, 128),
+    ([300, 1, 0, 2, 130, 513], 512, 256),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
@@ -182,7 +186,7 @@ def test_determinism_and_grouped_equals_per_expert():
     torch.cuda.synchronize()
     for p, q in ((h1, h1b), (a, ab), (y, yb), (ws, wsb), (dx, dxb)):
         assert torch.equal(p.view(torch.int16), q.view(torch.int16))
-    per = 3 * case.F * case.H
+    per = gg.packed_bytes(1, case.H, case.F) // 2     # one expert block is an E = 1 packed buffer
     for e in range(case.E):
         s, t = int(case.offsets[e]), int(case.offsets[e + 1])
         if s == t:
@@ -267,3 +271,27 @@ def test_workload_sampled_rows(name):
         if pad.stop > pad.start:
             assert int((y[pad].float() != 0).sum()) == 0 and int((dx[pad].float() != 0).sum()) == 0
     log(f"[sampled] {name} ok")
+
+
+def test_fragment_ordered_copies_layout():
+    """The packed buffer's fragment-ordered copies: block b of 32 weight rows
+    and k16 step s hold, for lane l, rows 32b + (l & 31) and k 16s + 8(l >> 5);
+    W1's blocks go gate, gate, up, up per 64 features."""
+    _gpu_ok()
+    import moe_expert_grouped_ragged_amd as gg
+    E, H, F = 3, 256, 128
+    case = workload.custom_case([1, 2, 3], H, F, seed=5)
+    w1, w2 = case.w1.cuda(), case.w2.cuda()
+    packed = gg.gg_pack_weights(w1, w2)
+    torch.cuda.synchronize()
+    assert packed.numel() == 6 * E * H * F
+    blk = packed.view(E, 6 * H * F)
+    for e in range(E):
+        assert torch.equal(blk[e, :2 * F * H].view(2 * F, H), w1[e])
+        assert torch.equal(blk[e, 2 * F * H:3 * F * H].view(H, F), w2[e])
+        # W1 rows in feature blocks of 64: gate rows then up rows
+        w1i = torch.cat([w1[e][:F].view(F // 64, 64, H), w1[e][F:].view(F // 64, 64, H)], 1).reshape(2 * F, H)
+        for got, w, K in ((blk[e, 3 * F * H:5 * F * H], w1i, H), (blk[e, 5 * F * H:], w2[e], F)):
+            n = w.shape[0]
+            want = w.reshape(n // 32, 32, K // 16, 2, 8).permute(0, 2, 3, 1, 4).reshape(-1)
+            assert torch.equal(got, want)
