@@ -77,10 +77,10 @@ const char* gg_status_string(int status);
 
 /* Bytes of the packed weight buffer.  Expert-major blocks: expert e's block
  * holds W1_e [2F][H] then W2_e [H][F], bf16 row-major.  When H % 256 == 0 and
- * F % 128 == 0 the block also holds, after them, copies of W1_e and W2_e in
- * MFMA fragment order (read by the forward tiles; written by gg_pack_weights):
- * 12*E*H*F bytes in all, 6*E*H*F otherwise.  One expert block is itself a
- * packed buffer with E = 1. */
+ * F % 128 == 0 the block also holds, after them, copies of W1_e, W2_e and
+ * W1_e^T in MFMA fragment order (read by the forward tiles and by the dX
+ * GEMM; written by gg_pack_weights): 16*E*H*F bytes in all, 6*E*H*F
+ * otherwise.  One expert block is itself a packed buffer with E = 1. */
 size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F);
 
 /* Bytes of the gg_dgrad workspace: dH1 [M][2F] bf16 = 4*M*F. */

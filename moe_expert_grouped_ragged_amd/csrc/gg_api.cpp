@@ -115,7 +115,7 @@ int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStre
 // the four-wave forward tiles.
 bool has_frag(int64_t H, int64_t F) { return H % 256 == 0 && F % 128 == 0; }
 // Elements of one expert block of the packed buffer.
-int64_t expert_block(int64_t H, int64_t F) { return (has_frag(H, F) ? 6 : 3) * F * H; }
+int64_t expert_block(int64_t H, int64_t F) { return (has_frag(H, F) ? 8 : 3) * F * H; }
 
 gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed, int64_t E,
                            int64_t H, int64_t F) {
@@ -364,6 +364,7 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
     q.N = static_cast<int>(H);
     q.ldw = static_cast<int>(H);
     q.out0 = static_cast<uint16_t*>(dx);
+    if (has_frag(H, F)) q.wfrag = static_cast<const uint16_t*>(packed) + 6 * F * H;   // W1^T fragments
     return gg::launch_dgrad_fc1(q, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 

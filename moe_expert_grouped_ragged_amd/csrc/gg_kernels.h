@@ -42,7 +42,7 @@ hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
-// Fragment-ordered copies of W1 and W2 inside every expert block (H % 256 == 0, F % 128 == 0).
+// Fragment-ordered copies of W1, W2 and W1^T inside every expert block (H % 256 == 0, F % 128 == 0).
 hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 // dprobs[r] = sum over g of part[r][g] in increasing g, for the routed rows.

@@ -1429,33 +1429,45 @@ void tile4_kernel(const GemmParams p) {
     }
 }
 
-// Fragment-ordered copies of every expert's W1 and W2 (layout above), written
-// from the row-major matrices of the same expert block.
+// Fragment-ordered copies (layout above) of every expert's W1 and W2 for the
+// forward tiles and of W1^T [H][2F] for dX = dH1 W1, written from the
+// row-major matrices of the same expert block (offsets 3FH, 5FH and 6FH).
 __global__ void pack_frag_kernel(uint16_t* __restrict__ packed, int E, int H, int F) {
-    const int64_t stride_e = 6LL * H * F;                 // elements per expert block
+    const int64_t stride_e = 8LL * H * F;                       // elements per expert block
     const int64_t c1 = 2LL * F * H / 8, c2 = 1LL * H * F / 8;   // 16-byte chunks per matrix
-    const int64_t total = static_cast<int64_t>(E) * (c1 + c2);
+    const int64_t per_e = 2 * c1 + c2;
+    const int64_t total = static_cast<int64_t>(E) * per_e;
     const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
-        const int e = static_cast<int>(i / (c1 + c2));
-        int64_t ci = i - static_cast<int64_t>(e) * (c1 + c2);
+        const int e = static_cast<int>(i / per_e);
+        int64_t ci = i - static_cast<int64_t>(e) * per_e;
         uint16_t* blk = packed + e * stride_e;
-        const bool second = ci >= c1;
-        if (second) ci -= c1;
-        const int K = second ? F : H;
+        const int which = ci < c1 ? 0 : (ci < c1 + c2 ? 1 : 2);   // W1, W2, W1^T
+        ci -= which == 0 ? 0 : (which == 1 ? c1 : c1 + c2);
+        const int K = which == 1 ? F : (which == 0 ? H : 2 * F);
         const int l = static_cast<int>(ci & 63);
         const int64_t rest = ci >> 6;
         const int ks = static_cast<int>(rest % (K / 16));
         const int rbk = static_cast<int>(rest / (K / 16));
+        const int k0 = ks * 16 + (l >> 5) * 8;
+        uint16_t* dst = blk + (which == 0 ? 3LL : (which == 1 ? 5LL : 6LL)) * F * H + ci * 8;
+        if (which == 2) {   // row h of W1^T is column h of W1
+            const int h = rbk * 32 + (l & 31);
+            uint16_t v[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = blk[static_cast<int64_t>(k0 + x) * H + h];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16),
+                                                        v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+            continue;
+        }
         int row;
-        if (second) {
+        if (which == 1) {
             row = rbk * 32 + (l & 31);
         } else {
             const int q = rbk & 3, fb = rbk >> 2;
             row = (q < 2 ? 0 : F) + fb * 64 + (q & 1) * 32 + (l & 31);
         }
-        const uint16_t* src = blk + (second ? 2LL * F * H : 0) + static_cast<int64_t>(row) * K + ks * 16 + (l >> 5) * 8;
-        uint16_t* dst = blk + (second ? 5LL * F * H : 3LL * F * H) + ci * 8;
+        const uint16_t* src = blk + (which == 1 ? 2LL * F * H : 0) + static_cast<int64_t>(row) * K + k0;
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
     }
 }
@@ -1537,7 +1549,7 @@ hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     return launch_tile4<EPI_STORE, false>(p, num_cu, s);
 }
 hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s) {
-    const int64_t chunks = static_cast<int64_t>(E) * 3 * H * F / 8;
+    const int64_t chunks = static_cast<int64_t>(E) * 5 * H * F / 8;
     int64_t blocks = (chunks + 255) / 256;
     if (blocks > 16384) blocks = 16384;
     if (blocks <= 0) return hipSuccess;
@@ -1549,7 +1561,12 @@ hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
                            : launch_cfg<true, EPI_DSWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s) {
-    return launch_cfg<true, EPI_STORE, false>(p, num_cu, s);
+    if (!p.wfrag) return launch_cfg<true, EPI_STORE, false>(p, num_cu, s);
+    GemmParams q = p;
+    q.stream_only = 1;
+    const hipError_t err = launch_cfg<true, EPI_STORE, false>(q, num_cu, s);
+    if (err != hipSuccess) return err;
+    return launch_tile4<EPI_STORE, false>(p, num_cu, s);   // W1^T fragments: same K-contiguous form
 }
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
                             hipStream_t s) {

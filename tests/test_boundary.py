@@ -52,7 +52,7 @@ def test_size_helpers():
     assert gg.dgrad_workspace_bytes(512, 128) == 4 * 512 * 128
     assert gg.packed_bytes(0, 64, 128) == 0
     # H % 256 == 0 and F % 128 == 0: each expert block also holds fragment-ordered copies
-    assert gg.packed_bytes(2, 256, 128) == 12 * 2 * 256 * 128
+    assert gg.packed_bytes(2, 256, 128) == 16 * 2 * 256 * 128
     assert gg.packed_bytes(2, 256, 64) == 6 * 2 * 256 * 64
     assert gg.packed_bytes(2, 384, 128) == 6 * 2 * 384 * 128
     assert gg.lib.gg_status_string(5) == b"GG_ERR_ALIASING"

@@ -276,7 +276,7 @@ def test_workload_sampled_rows(name):
 def test_fragment_ordered_copies_layout():
     """The packed buffer's fragment-ordered copies: block b of 32 weight rows
     and k16 step s hold, for lane l, rows 32b + (l & 31) and k 16s + 8(l >> 5);
-    W1's blocks go gate, gate, up, up per 64 features."""
+    W1's blocks go gate, gate, up, up per 64 features; the third copy is W1^T."""
     _gpu_ok()
     import moe_expert_grouped_ragged_amd as gg
     E, H, F = 3, 256, 128
@@ -284,14 +284,15 @@ def test_fragment_ordered_copies_layout():
     w1, w2 = case.w1.cuda(), case.w2.cuda()
     packed = gg.gg_pack_weights(w1, w2)
     torch.cuda.synchronize()
-    assert packed.numel() == 6 * E * H * F
-    blk = packed.view(E, 6 * H * F)
+    assert packed.numel() == 8 * E * H * F
+    blk = packed.view(E, 8 * H * F)
     for e in range(E):
         assert torch.equal(blk[e, :2 * F * H].view(2 * F, H), w1[e])
         assert torch.equal(blk[e, 2 * F * H:3 * F * H].view(H, F), w2[e])
         # W1 rows in feature blocks of 64: gate rows then up rows
         w1i = torch.cat([w1[e][:F].view(F // 64, 64, H), w1[e][F:].view(F // 64, 64, H)], 1).reshape(2 * F, H)
-        for got, w, K in ((blk[e, 3 * F * H:5 * F * H], w1i, H), (blk[e, 5 * F * H:], w2[e], F)):
+        for got, w, K in ((blk[e, 3 * F * H:5 * F * H], w1i, H), (blk[e, 5 * F * H:6 * F * H], w2[e], F),
+                          (blk[e, 6 * F * H:], w1[e].t().contiguous(), 2 * F)):
             n = w.shape[0]
             want = w.reshape(n // 32, 32, K // 16, 2, 8).permute(0, 2, 3, 1, 4).reshape(-1)
             assert torch.equal(got, want)
