@@ -89,7 +89,7 @@ def _run(layout, R, base, weighted=False):
 
 @pytest.mark.parametrize("weighted", [False, True], ids=["swiglu", "weighted_qgeglu"])
 @pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64), (136, 200, 96),
-                                   (256, 128, 40), (256, 128, 96)])   # the last two: four-wave tiles
+                                   (256, 128, 40), (256, 128, 96), (256, 256, 64)])   # the last three: four-wave tiles
 def test_rows_are_batch_invariant(H, F, R, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

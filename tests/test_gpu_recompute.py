@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 CASES = [([5, 0, 7, 33], 64, 64), ([31, 32, 63, 64, 65, 0, 1], 136, 200), ([300, 0, 257, 40, 1], 128, 96),
          ([96, 95, 352, 0], 136, 200),
          # four-wave forward tiles; the recompute's H1 comes from the eight-wave plain GEMM
-         ([300, 0, 257, 40, 1, 97], 256, 128)]
+         ([300, 0, 257, 40, 1, 97], 256, 128),
+         ([300, 0, 257, 40, 1, 97], 256, 256)]
 MODES = [("swiglu", False), ("qgeglu", True)]
 
 
