@@ -35,7 +35,8 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DEFAULT_WORKLOAD = "uniform_e32_h2048_f768"
 KERNEL_SOURCES = ["moe_expert_grouped_ragged_amd/csrc/gg_kernels.hip",
-                  "moe_expert_grouped_ragged_amd/csrc/gg_kernels.h"]
+                  "moe_expert_grouped_ragged_amd/csrc/gg_kernels.h",
+                  "moe_expert_grouped_ragged_amd/csrc/gg_api.cpp"]   # which kernels a call launches
 
 
 def kernel_source_hash() -> str:

@@ -98,6 +98,7 @@ def test_tiny_workload():
     ([17, 0, 255, 256, 257, 600, 97, 96], 256, 128),
     ([300, 1, 0, 2, 130, 513], 512, 256),
     ([0, 700, 129, 0, 256], 256, 512),
+    ([130, 0, 513, 40], 256, 1024),   # FC2 on four-wave tiles from F = 1024
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
