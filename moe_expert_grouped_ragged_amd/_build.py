@@ -21,7 +21,8 @@ HEADERS = ["gg_kernels.h"]
 # Packed-fp32 VALU ops are disabled for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
              "-Wall", "-Werror", "-Wno-unused-command-line-argument",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wl,-z,defs"]   # every symbol resolved at link time
 
 
 def hipcc() -> str:

@@ -36,6 +36,7 @@ struct GemmParams {
     // expert stride), or null.  With it, the tiles run in a four-wave launch.
     const uint16_t* wfrag;
     int stream_only;           // run only the streaming items (tiles launched separately)
+    int absorb_slots;          // grid of the separate tile launch, or 0 (see build_schedule)
 };
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);

@@ -186,9 +186,16 @@ __device__ __forceinline__ bool streams_rows(int m) { return m > 0 && tile_rows_
 // flavors: s_pre counts 256x256 tiles of the large experts, s_spre counts
 // streaming items of the small ones.  Offsets are clamped into [0, M] so that
 // bad offsets cannot index out of bounds.
+//
+// absorb_slots > 0 (the grid of a separate tile launch): when covering every
+// row with tiles (the short remainders as partial tiles) takes no more rounds
+// of absorb_slots workgroups than the split does, every row goes to the tiles
+// and there are no streaming items.  Every workgroup of both launches takes
+// the same decision from the same offsets.
 template <int NT>
 __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M,
-                                               int tiles_n, int items_n, int* s_off, int* s_pre, int* s_spre) {
+                                               int tiles_n, int items_n, int absorb_slots, int* s_off,
+                                               int* s_pre, int* s_spre) {
     const int tid = threadIdx.x;
     for (int e = tid; e <= E; e += NT) {
         int64_t o = offsets[e];
@@ -201,8 +208,25 @@ __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offse
         const int per = (E + 63) / 64;
         const int e0 = lane * per;
         const int e1 = min(E, e0 + per);
-        auto big = [&](int e) { return tiles_m_of(max(0, s_off[e + 1] - s_off[e])) * tiles_n; };
-        auto small = [&](int e) { return streams_rows(max(0, s_off[e + 1] - s_off[e])) ? items_n : 0; };
+        auto rows = [&](int e) { return max(0, s_off[e + 1] - s_off[e]); };
+        bool absorb = false;
+        if (absorb_slots > 0) {
+            int split = 0, all = 0;
+            for (int e = e0; e < e1; ++e) {
+                split += tiles_m_of(rows(e));
+                all += (rows(e) + 255) / 256;
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                split += __shfl_xor(split, d, 64);
+                all += __shfl_xor(all, d, 64);
+            }
+            const int64_t r_split = (static_cast<int64_t>(split) * tiles_n + absorb_slots - 1) / absorb_slots;
+            const int64_t r_all = (static_cast<int64_t>(all) * tiles_n + absorb_slots - 1) / absorb_slots;
+            absorb = all > split && r_all <= r_split;
+        }
+        auto big = [&](int e) { return (absorb ? (rows(e) + 255) / 256 : tiles_m_of(rows(e))) * tiles_n; };
+        auto small = [&](int e) { return (!absorb && streams_rows(rows(e))) ? items_n : 0; };
         int sum = 0, ssum = 0;
         for (int e = e0; e < e1; ++e) {
             sum += big(e);
@@ -290,7 +314,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     constexpr int S_COLS = (EPI == EPI_SWIGLU) ? S_ROWS / 2 : S_ROWS;
     const int items_n = (N + S_COLS - 1) / S_COLS;
     static_assert(TBM == 256, "tile_rows_of assumes 256-row tiles");
-    build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, s_off, s_pre, s_spre);
+    build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, p.absorb_slots, s_off, s_pre, s_spre);
     const int n_items = uni(s_spre[E]);
 
     const int tid = threadIdx.x;
@@ -1241,7 +1265,8 @@ void tile4_kernel(const GemmParams p) {
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 96 : 192;     // streaming items (counted, not run here)
     const int tiles_n = N / TILE_COLS;
-    build_schedule<T4_THREADS>(p.offsets, E, M, tiles_n, (N + S_COLS - 1) / S_COLS, s_off, s_pre, s_spre);
+    build_schedule<T4_THREADS>(p.offsets, E, M, tiles_n, (N + S_COLS - 1) / S_COLS, p.absorb_slots, s_off, s_pre,
+                               s_spre);
     const int n_tiles = uni(s_pre[E]);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1265,7 +1290,7 @@ void tile4_kernel(const GemmParams p) {
         const int local = t - uni(s_pre[e]);
         const int rb = uni(s_off[e]);
         const int row_end = uni(s_off[e + 1]);
-        const int tiles_m = tiles_m_of(row_end - rb);
+        const int tiles_m = uni((s_pre[e + 1] - s_pre[e]) / tiles_n);   // either tile rule
         const int row0 = uni(rb + (local % tiles_m) * TBM);
         const int col0 = uni((local / tiles_m) * TILE_COLS);
         const int rows = min(TBM, row_end - row0);
@@ -1514,15 +1539,30 @@ static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream
 
 static bool plain_swiglu(const GemmParams& p) { return p.slope == 1.0f && !p.probs && !p.dp_part; }
 
-template <int EPI, bool EXT>
-static hipError_t launch_tile4(const GemmParams& p, int num_cu, hipStream_t stream) {
+template <int EPI>
+static int64_t tile4_grid(const GemmParams& p, int num_cu) {
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int64_t tiles_n = p.N / TILE_COLS;
+    // upper bound of sum_e ceil(m_e / 256) tiles without reading the offsets
     const int64_t tiles_m_max = (static_cast<int64_t>(p.M) + static_cast<int64_t>(p.E) * (TBM - 1)) / TBM;
-    int64_t grid = num_cu;
-    if (tiles_m_max * tiles_n < grid) grid = tiles_m_max * tiles_n;
+    return tiles_m_max * tiles_n < num_cu ? tiles_m_max * tiles_n : num_cu;
+}
+
+// The split call: the 256-row tiles in the four-wave kernel and the streaming
+// items in the eight-wave kernel (stream_only), both on s.  Both launches get
+// the tile grid as absorb_slots, so they agree on which rows the tiles take.
+template <int EPI, bool EXT>
+static hipError_t launch_split(const GemmParams& p, int num_cu, hipStream_t s) {
+    const int64_t grid = tile4_grid<EPI>(p, num_cu);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((tile4_kernel<EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, stream, p);
+    GemmParams q = p;
+    q.absorb_slots = static_cast<int>(grid);
+    q.stream_only = 1;
+    constexpr bool W_KN = false;
+    hipError_t err = launch_cfg<W_KN, EPI, EXT>(q, num_cu, s);
+    if (err != hipSuccess) return err;
+    q.stream_only = 0;
+    hipLaunchKernelGGL((tile4_kernel<EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, s, q);
     return hipGetLastError();
 }
 
@@ -1533,20 +1573,11 @@ hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag)
         return plain ? launch_cfg<false, EPI_SWIGLU, false>(p, num_cu, s)
                      : launch_cfg<false, EPI_SWIGLU, true>(p, num_cu, s);
-    GemmParams q = p;
-    q.stream_only = 1;
-    hipError_t err = plain ? launch_cfg<false, EPI_SWIGLU, false>(q, num_cu, s)
-                           : launch_cfg<false, EPI_SWIGLU, true>(q, num_cu, s);
-    if (err != hipSuccess) return err;
-    return plain ? launch_tile4<EPI_SWIGLU, false>(p, num_cu, s) : launch_tile4<EPI_SWIGLU, true>(p, num_cu, s);
+    return plain ? launch_split<EPI_SWIGLU, false>(p, num_cu, s) : launch_split<EPI_SWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag) return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
-    GemmParams q = p;
-    q.stream_only = 1;
-    const hipError_t err = launch_cfg<false, EPI_STORE, false>(q, num_cu, s);
-    if (err != hipSuccess) return err;
-    return launch_tile4<EPI_STORE, false>(p, num_cu, s);
+    return launch_split<EPI_STORE, false>(p, num_cu, s);
 }
 hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s) {
     const int64_t chunks = static_cast<int64_t>(E) * 5 * H * F / 8;
@@ -1562,11 +1593,18 @@ hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
 }
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag) return launch_cfg<true, EPI_STORE, false>(p, num_cu, s);
+    // the tiles read W1^T fragments (the same K-contiguous form as the forward
+    // copies); the streaming items read W1 transposed in the eight-wave kernel
+    const int64_t grid = tile4_grid<EPI_STORE>(p, num_cu);
+    if (grid <= 0) return hipSuccess;
     GemmParams q = p;
+    q.absorb_slots = static_cast<int>(grid);
     q.stream_only = 1;
-    const hipError_t err = launch_cfg<true, EPI_STORE, false>(q, num_cu, s);
+    hipError_t err = launch_cfg<true, EPI_STORE, false>(q, num_cu, s);
     if (err != hipSuccess) return err;
-    return launch_tile4<EPI_STORE, false>(p, num_cu, s);   // W1^T fragments: same K-contiguous form
+    q.stream_only = 0;
+    hipLaunchKernelGGL((tile4_kernel<EPI_STORE, false>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, s, q);
+    return hipGetLastError();
 }
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
                             hipStream_t s) {

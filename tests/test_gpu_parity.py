@@ -99,6 +99,9 @@ def test_tiny_workload():
     ([300, 1, 0, 2, 130, 513], 512, 256),
     ([0, 700, 129, 0, 256], 256, 512),
     ([130, 0, 513, 40], 256, 1024),   # FC2 on four-wave tiles from F = 1024
+    # 279 small experts and 17 of 512 rows: taking the small ones as partial
+    # tiles would add a round, so they stay streaming items beside the tiles
+    ([512 if i % 18 == 0 else 40 for i in range(296)], 256, 128),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
