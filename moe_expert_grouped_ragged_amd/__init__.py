@@ -169,7 +169,7 @@ def expert_views(packed: torch.Tensor, E: int, H: int, F: int):
     so that the derived fragment-ordered copies follow."""
     per = packed_bytes(1, H, F) // 2
     w1 = [packed[e * per:e * per + 2 * F * H].view(2 * F, H) for e in range(E)]
-    w2 = [packed[e * per + 2 * F * H:(e + 1) * per].view(H, F) for e in range(E)]
+    w2 = [packed[e * per + 2 * F * H:e * per + 3 * F * H].view(H, F) for e in range(E)]
     return w1, w2
 
 

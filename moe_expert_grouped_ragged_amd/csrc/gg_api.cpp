@@ -111,8 +111,8 @@ int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStre
     return GG_OK;
 }
 
-// Shapes whose packed buffer also holds the fragment-ordered copies read by
-// the four-wave forward tiles.
+// Shapes whose packed buffer also holds the fragment-ordered copies (W1, W2,
+// W1^T) read by the four-wave tiles of FC1, FC2 and dX.
 bool has_frag(int64_t H, int64_t F) { return H % 256 == 0 && F % 128 == 0; }
 // Elements of one expert block of the packed buffer.
 int64_t expert_block(int64_t H, int64_t F) { return (has_frag(H, F) ? 8 : 3) * F * H; }

@@ -102,6 +102,9 @@ def test_tiny_workload():
     # 279 small experts and 17 of 512 rows: taking the small ones as partial
     # tiles would add a round, so they stay streaming items beside the tiles
     ([512 if i % 18 == 0 else 40 for i in range(296)], 256, 128),
+    # the maximum expert count with fragment copies: the four-wave tiles find
+    # their expert among 1024 beside the streaming launch
+    ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 256, 128),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
@@ -206,16 +209,19 @@ def test_determinism_and_grouped_equals_per_expert():
         assert torch.equal(dxe.view(torch.int16), dx[s:t].view(torch.int16))
 
 
-def test_repack_after_middle_expert_replaced():
+@pytest.mark.parametrize("H,F,counts", [(64, 64, [20, 30, 40]),
+                                         # fragment-ordered copies: re-packing rewrites them too
+                                         (256, 128, [120, 300, 40])])
+def test_repack_after_middle_expert_replaced(H, F, counts):
     _gpu_ok()
     import moe_expert_grouped_ragged_amd as gg
-    case = workload.custom_case([20, 30, 40], 64, 64, seed=17)
+    case = workload.custom_case(counts, H, F, seed=17)
     dc = DeviceCase(case)
     w1v, w2v = gg.expert_views(dc.packed, case.E, case.H, case.F)
     # views into the packed buffer re-pack as a no-op
     gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
     y0 = dc.forward()[2].clone()
-    new_w1 = workload.custom_case([1], 64, 64, seed=99).w1[0].cuda()
+    new_w1 = workload.custom_case([1], H, F, seed=99).w1[0].cuda()
     w1v = list(w1v)
     w1v[1] = new_w1                       # the middle expert is replaced by a new tensor
     gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
