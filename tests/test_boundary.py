@@ -151,3 +151,22 @@ def test_python_binding_refuses_unsupported_weights():
     w2 = torch.zeros(2, 8, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="frozen"):
         gg.gg_pack_weights(w1, w2)
+
+
+def test_expert_views_slice_each_block():
+    """expert_views: W1_e at e*block, W2_e right after it, where one expert
+    block also holds the fragment-ordered copies when H % 256 == 0 and
+    F % 128 == 0 (host-side slicing only; a CPU tensor stands in for the
+    packed buffer)."""
+    import torch
+    gg = _gg()
+    for E, H, F in ((3, 64, 64), (3, 256, 128), (2, 512, 256)):
+        n = gg.packed_bytes(E, H, F) // 2
+        block = n // E
+        assert block == (8 if (H % 256 == 0 and F % 128 == 0) else 3) * F * H
+        packed = torch.arange(n, dtype=torch.int64)
+        w1, w2 = gg.expert_views(packed, E, H, F)
+        for e in range(E):
+            assert w1[e].shape == (2 * F, H) and w2[e].shape == (H, F)
+            assert int(w1[e][0, 0]) == e * block and int(w1[e][-1, -1]) == e * block + 2 * F * H - 1
+            assert int(w2[e][0, 0]) == e * block + 2 * F * H and int(w2[e][-1, -1]) == e * block + 3 * F * H - 1
