@@ -318,19 +318,17 @@ def main():
     n_live = int(np.count_nonzero(np.diff(case.offsets)))
     bfwd, bdg = algorithmic_bytes(M, H, F, n_live)
     # dominant kernel: the FC1 grouped GEMM with the SwiGLU epilogue (the
-    # largest share of the step), timed per gg_forward_fc1_swiglu call.  When
-    # the packed buffer holds fragment-ordered weights (H % 256 == 0 and
-    # F % 128 == 0) the call is two launches on the stream: the streaming items
-    # (eight-wave kernel), then the 256-row tiles (four-wave kernel); the record
-    # covers both.  Algorithmic work per call: 4*M*H*F FLOPs; HBM bytes = X read
-    # (2MH) + W1 of the experts with rows (4HF each) + H1 and A written (4MF +
-    # 2MF).  The bound is whichever of MFMA time and HBM time is larger.
+    # largest share of the step), one launch per gg_forward_fc1_swiglu call:
+    # the four-wave kernel when the packed buffer holds fragment-ordered
+    # weights (H % 256 == 0 and F % 128 == 0), else the eight-wave kernel.
+    # Algorithmic work per launch: 4*M*H*F FLOPs; HBM bytes = X read (2MH) +
+    # W1 of the experts with rows (4HF each) + H1 and A written (4MF + 2MF).
+    # The bound is whichever of MFMA time and HBM time is larger.
     fc1_flops = 4.0 * M * H * F
     fc1_bytes = 2.0 * M * H + 4.0 * H * F * n_live + 6.0 * M * F
     fc1_ms = call_ms["fc1"]
-    two = H % 256 == 0 and F % 128 == 0
-    kname = ("FC1+SwiGLU call: tile4_kernel<SwiGLU> (256-row tiles) + grouped_gemm_kernel<FC1+SwiGLU> "
-             "(streaming items)" if two else "grouped_gemm_kernel<FC1+SwiGLU>")
+    four = H % 256 == 0 and F % 128 == 0
+    kname = "tile4_kernel<SwiGLU>" if four else "grouped_gemm_kernel<FC1+SwiGLU>"
     mfma_bound = fc1_flops / (PEAK_BF16_TFLOPS * 1e12) >= fc1_bytes / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
@@ -340,8 +338,7 @@ def main():
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
         roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
-    roof.update({"traffic": None if glu else load_traffic(args.workload, "fc1"), "launches": 2 if two else 1,
-                 "avg_launch_ms": fc1_ms,
+    roof.update({"traffic": None if glu else load_traffic(args.workload, "fc1"), "avg_launch_ms": fc1_ms,
                  "flops_per_launch": fc1_flops, "algorithmic_bytes_per_launch": fc1_bytes})
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

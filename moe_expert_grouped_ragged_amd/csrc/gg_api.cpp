@@ -281,9 +281,7 @@ int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void*
     p.N = static_cast<int>(H);
     p.ldw = static_cast<int>(F);
     p.out0 = static_cast<uint16_t*>(y);
-    // Below F = 1024 the K loop is short enough that the separate launch for
-    // the streaming items costs more than the four-wave tiles save.
-    if (has_frag(H, F) && F >= 1024) p.wfrag = static_cast<const uint16_t*>(packed) + 5 * F * H;
+    if (has_frag(H, F)) p.wfrag = static_cast<const uint16_t*>(packed) + 5 * F * H;
     return gg::launch_fc2(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 

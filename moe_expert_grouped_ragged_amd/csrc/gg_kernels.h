@@ -32,11 +32,9 @@ struct GemmParams {
     float* dp_part;            // derivative variant: partial sums of dp per row and
                                // 32-column group [M][dp_ld], or null
     int dp_ld;                 // ceil(N / 32)
-    // Forward GEMMs: this GEMM's matrix in the fragment-ordered copy (same
-    // expert stride), or null.  With it, the tiles run in a four-wave launch.
+    // FC1, FC2 and dX: this GEMM's matrix in the fragment-ordered copy (same
+    // expert stride), or null.  With it, the GEMM runs in the four-wave kernel.
     const uint16_t* wfrag;
-    int stream_only;           // run only the streaming items (tiles launched separately)
-    int absorb_slots;          // grid of the separate tile launch, or 0 (see build_schedule)
 };
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);

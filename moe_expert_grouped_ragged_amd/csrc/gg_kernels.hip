@@ -7,7 +7,11 @@
 // request, section "Summary"), and then walks the global tile list.  Experts
 // with no rows own no tiles, so their weights are never read.
 //
-// Two flavors share one launch.  Rows that fill 256-row tiles run as 256 x 256
+// Two kernels.  The eight-wave kernel (grouped_gemm_kernel) runs every GEMM
+// whose packed buffer has no fragment-ordered copies, and always the dgrad
+// FC2; the four-wave kernel (tile4_kernel, below) runs FC1, FC2 and dX over
+// those copies.  In the eight-wave kernel two flavors share one launch.  Rows
+// that fill 256-row tiles run as 256 x 256
 // output tiles; the at most 96 rows an expert leaves over (all rows of a
 // small expert) run as weight-streaming items, before the tiles.  An item is
 // those rows x 192 weight rows (six compute waves of 32 rows; two more waves
@@ -186,16 +190,9 @@ __device__ __forceinline__ bool streams_rows(int m) { return m > 0 && tile_rows_
 // flavors: s_pre counts 256x256 tiles of the large experts, s_spre counts
 // streaming items of the small ones.  Offsets are clamped into [0, M] so that
 // bad offsets cannot index out of bounds.
-//
-// absorb_slots > 0 (the grid of a separate tile launch): when covering every
-// row with tiles (the short remainders as partial tiles) takes no more rounds
-// of absorb_slots workgroups than the split does, every row goes to the tiles
-// and there are no streaming items.  Every workgroup of both launches takes
-// the same decision from the same offsets.
 template <int NT>
 __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offsets, int E, int M,
-                                               int tiles_n, int items_n, int absorb_slots, int* s_off,
-                                               int* s_pre, int* s_spre) {
+                                               int tiles_n, int items_n, int* s_off, int* s_pre, int* s_spre) {
     const int tid = threadIdx.x;
     for (int e = tid; e <= E; e += NT) {
         int64_t o = offsets[e];
@@ -209,24 +206,8 @@ __device__ __forceinline__ void build_schedule(const int64_t* __restrict__ offse
         const int e0 = lane * per;
         const int e1 = min(E, e0 + per);
         auto rows = [&](int e) { return max(0, s_off[e + 1] - s_off[e]); };
-        bool absorb = false;
-        if (absorb_slots > 0) {
-            int split = 0, all = 0;
-            for (int e = e0; e < e1; ++e) {
-                split += tiles_m_of(rows(e));
-                all += (rows(e) + 255) / 256;
-            }
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                split += __shfl_xor(split, d, 64);
-                all += __shfl_xor(all, d, 64);
-            }
-            const int64_t r_split = (static_cast<int64_t>(split) * tiles_n + absorb_slots - 1) / absorb_slots;
-            const int64_t r_all = (static_cast<int64_t>(all) * tiles_n + absorb_slots - 1) / absorb_slots;
-            absorb = all > split && r_all <= r_split;
-        }
-        auto big = [&](int e) { return (absorb ? (rows(e) + 255) / 256 : tiles_m_of(rows(e))) * tiles_n; };
-        auto small = [&](int e) { return (!absorb && streams_rows(rows(e))) ? items_n : 0; };
+        auto big = [&](int e) { return tiles_m_of(rows(e)) * tiles_n; };
+        auto small = [&](int e) { return streams_rows(rows(e)) ? items_n : 0; };
         int sum = 0, ssum = 0;
         for (int e = e0; e < e1; ++e) {
             sum += big(e);
@@ -314,7 +295,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     constexpr int S_COLS = (EPI == EPI_SWIGLU) ? S_ROWS / 2 : S_ROWS;
     const int items_n = (N + S_COLS - 1) / S_COLS;
     static_assert(TBM == 256, "tile_rows_of assumes 256-row tiles");
-    build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, p.absorb_slots, s_off, s_pre, s_spre);
+    build_schedule<NTHREADS>(p.offsets, E, M, tiles_n, items_n, s_off, s_pre, s_spre);
     const int n_items = uni(s_spre[E]);
 
     const int tid = threadIdx.x;
@@ -902,7 +883,7 @@ void grouped_gemm_kernel(const GemmParams p) {
     // ---- streaming flavor first (work items [0, n_stream)), then the tiles
     int t = slot;
     if (t < n_stream) t = uni(stream_items(t));
-    const int n_tiles = p.stream_only ? 0 : uni(s_pre[E]);   // tiles of a separate launch
+    const int n_tiles = uni(s_pre[E]);
     for (int tt = t - n_stream; tt < n_tiles; tt += G) {
         setup_tile(tt);
 #pragma unroll
@@ -1203,10 +1184,12 @@ void grouped_gemm_kernel(const GemmParams p) {
     }
 }
 
-// ---------------------------------------------------------------- four-wave tiles
+// ---------------------------------------------------------------- four-wave kernel
 //
-// Forward tiles over a fragment-ordered copy of the weights (present in the
-// packed buffer when H % 256 == 0 and F % 128 == 0).  Four waves compute a
+// FC1, FC2 and dX over a fragment-ordered copy of the weights (present in the
+// packed buffer when H % 256 == 0 and F % 128 == 0), all in one launch: first
+// thin items (the at most 96 rows an expert leaves after its 256-row tiles,
+// or all rows of a small expert), then the tiles.  Four waves compute a
 // 256 x 256 tile: wave w owns token rows (w >> 1) * 128 .. +127 and weight rows
 // (w & 1) * 128 .. +127, as 4 x 4 accumulator blocks of 32 x 32 (all 256
 // AGPRs).  Tokens stream through a 4-slot LDS ring of 64-k stages by LDS-DMA,
@@ -1247,6 +1230,10 @@ __device__ __forceinline__ void wfrag_load(bf16x8& w, const uint16_t* ptr) {
 __device__ __forceinline__ void wfrag_wait38(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
     asm volatile("s_waitcnt vmcnt(38)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
 }
+// The same for a thin item's step (two weight blocks, 19 later loads).
+__device__ __forceinline__ void wfrag_wait19(bf16x8& a, bf16x8& b) {
+    asm volatile("s_waitcnt vmcnt(19)" : "+v"(a), "+v"(b) :: "memory");
+}
 __device__ __forceinline__ void wfrag_hold(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
     asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
 }
@@ -1263,10 +1250,11 @@ void tile4_kernel(const GemmParams p) {
     __shared__ int s_spre[GG_KMAX_EXPERTS + 1];
     const int E = p.E, M = p.M, K = p.K, N = p.N;
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
-    constexpr int S_COLS = (EPI == EPI_SWIGLU) ? 96 : 192;     // streaming items (counted, not run here)
     const int tiles_n = N / TILE_COLS;
-    build_schedule<T4_THREADS>(p.offsets, E, M, tiles_n, (N + S_COLS - 1) / S_COLS, p.absorb_slots, s_off, s_pre,
-                               s_spre);
+    // thin items (the at most 96 rows an expert leaves after its tiles) use
+    // the tiles' column blocks
+    build_schedule<T4_THREADS>(p.offsets, E, M, tiles_n, tiles_n, s_off, s_pre, s_spre);
+    const int n_items = uni(s_spre[E]);
     const int n_tiles = uni(s_pre[E]);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1285,12 +1273,171 @@ void tile4_kernel(const GemmParams p) {
     bf16x8 wr[8][4];
     bf16x8 tf[2][4];
 
-    for (int t = slot; t < n_tiles; t += G) {
+    // ---- thin items first: rows x TILE_COLS output columns.  Each wave owns
+    // two 32-row weight blocks (for SwiGLU the gate and up rows of 32
+    // features) against three 32-row token blocks.  Per k16 step: two weight
+    // loads seven steps ahead and one of the four token copies of the stage
+    // three stages ahead (128 rows, the ones past the item clamped), so a
+    // step's weights are complete at vmcnt(19) and a stage's tokens at
+    // vmcnt(24).
+    int wi = slot;
+    for (; wi < n_items; wi += G) {
+        const int e = uni(find_expert(s_spre, E, wi));
+        const int local = wi - uni(s_spre[e]);
+        const int rb = uni(s_off[e]);
+        const int re = uni(s_off[e + 1]);
+        const int row0 = uni(rb + tile_rows_of(re - rb));
+        const int rows = re - row0;                          // 1 .. 96
+        const int col0 = uni(local * TILE_COLS);
+        const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
+        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.w_expert_stride;
+        const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
+        const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : tb0 + 1;
+        auto wp = [&](int g, int j) -> const uint16_t* {
+            return wfe + ((static_cast<int64_t>(j ? tb1 : tb0) * nsteps + g) * 64 + lane) * 8;
+        };
+        auto tdma1 = [&](int s, int part) {
+            const int ss = s < kiters ? s : kiters - 1;
+            const int r = min((tid >> 3) + 32 * part, rows - 1);
+            const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * part) * 16;
+            dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
+        };
+        auto rd3 = [&](int g, int buf) {
+            const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
+            const int ch = 2 * (g & 3) + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
+        };
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+#pragma unroll
+        for (int g = -12; g < 0; ++g) {
+            const int gw = g + 7;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wfrag_load(wr[(gw + 8) & 7][j], wp(gw < 0 ? 0 : gw, j));
+            tdma1((g >> 2) + 3, g & 3);
+        }
+        for (int g0 = 0; g0 < nsteps; g0 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int g = g0 + u;
+                const int j4 = u & 3;
+                if (j4 == 0) {
+                    wait_vmcnt<24>();
+                    block_barrier();
+                    rd3(g, u & 1);
+                }
+                if (j4 < 3) rd3(g + 1, (u + 1) & 1);
+                wfrag_wait19(wr[u][0], wr[u][1]);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
+                const int gw = g + 7;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j));
+                tdma1((g >> 2) + 3, j4);
+            }
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) wfrag_hold(wr[s][0], wr[s][1], wr[s][2], wr[s][3]);
+        block_barrier();
+        mfma_drain();
+        int opaque = 0;
+        asm volatile("" : "+s"(opaque));
+        const int trow0 = row0 + opaque;
+        uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
+        if constexpr (EPI == EPI_STORE) {
+            // [96 rows][64 cols] bf16; 16-byte chunk c of row r at c ^ (r & 7)
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = i * 32 + (lane & 31);
+                        const int c = j * 4 + q;
+                        uint2 v;
+                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                        *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5)) = v;
+                    }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int gcol0 = col0 + 64 * wave;
+#pragma unroll 4
+            for (int sidx = 0; sidx < 12; ++sidx) {
+                const int idx = sidx * 64 + lane;
+                const int r = idx >> 3, c = idx & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (r & 7)) << 3));
+                if (r < rows)
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + gcol0 + c * 8) = v;
+            }
+        } else {
+            // [96 rows][32 features] bf16 arrays for A, gate and up; 16-byte
+            // chunk c of row r at c ^ (r & 3)
+            uint16_t* sA = stg;
+            uint16_t* sG = stg + 3072;
+            uint16_t* sU = stg + 6144;
+            const int fcol0 = col0 + 32 * wave;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int r = i * 32 + (lane & 31);
+                const float pr = (probs && r < rows) ? probs[trow0 + r] : 1.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (lane >> 5);
+                    uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
+                        ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
+                        const float gv = bf2f(gb[x]);
+                        const float uv = bf2f(ub[x]);
+                        const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
+                        const float v = sg * uv;
+                        ab[x] = f2bf(probs ? pr * v : v);
+                    }
+                    *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                    *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                    *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+            for (int sidx = 0; sidx < 6; ++sidx) {
+                const int idx = sidx * 64 + lane;
+                const int r = idx >> 2, c = idx & 3;
+                const int off = r * 32 + ((c ^ (r & 3)) << 3);
+                const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
+                const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                if (r < rows) {
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + fcol0 + c * 8) = va;
+                    if (p.out1) {
+                        uint16_t* h = p.out1 + static_cast<int64_t>(trow0 + r) * (2 * N) + fcol0 + c * 8;
+                        *reinterpret_cast<uint4*>(h) = vg;
+                        *reinterpret_cast<uint4*>(h + N) = vu;
+                    }
+                }
+            }
+        }
+        block_barrier();   // staging reads done before the next copies land
+    }
+
+    // ---- then the 256-row tiles
+    for (int t = wi - n_items; t < n_tiles; t += G) {
         const int e = uni(find_expert(s_pre, E, t));
         const int local = t - uni(s_pre[e]);
         const int rb = uni(s_off[e]);
         const int row_end = uni(s_off[e + 1]);
-        const int tiles_m = uni((s_pre[e + 1] - s_pre[e]) / tiles_n);   // either tile rule
+        const int tiles_m = tiles_m_of(row_end - rb);
         const int row0 = uni(rb + (local % tiles_m) * TBM);
         const int col0 = uni((local / tiles_m) * TILE_COLS);
         const int rows = min(TBM, row_end - row0);
@@ -1539,45 +1686,33 @@ static hipError_t launch_cfg(const GemmParams& p, int num_cu, hipStream_t stream
 
 static bool plain_swiglu(const GemmParams& p) { return p.slope == 1.0f && !p.probs && !p.dp_part; }
 
-template <int EPI>
-static int64_t tile4_grid(const GemmParams& p, int num_cu) {
+// One four-wave launch: thin items, then tiles.  Grid: one workgroup per CU,
+// or fewer when M and E bound the work below that.
+template <int EPI, bool EXT>
+static hipError_t launch_tile4(const GemmParams& p, int num_cu, hipStream_t stream) {
     constexpr int TILE_COLS = (EPI == EPI_SWIGLU) ? TBN / 2 : TBN;
     const int64_t tiles_n = p.N / TILE_COLS;
-    // upper bound of sum_e ceil(m_e / 256) tiles without reading the offsets
+    // upper bound of sum_e ceil(m_e / 256) tiles, plus one thin item per expert and column block
     const int64_t tiles_m_max = (static_cast<int64_t>(p.M) + static_cast<int64_t>(p.E) * (TBM - 1)) / TBM;
-    return tiles_m_max * tiles_n < num_cu ? tiles_m_max * tiles_n : num_cu;
-}
-
-// The split call: the 256-row tiles in the four-wave kernel and the streaming
-// items in the eight-wave kernel (stream_only), both on s.  Both launches get
-// the tile grid as absorb_slots, so they agree on which rows the tiles take.
-template <int EPI, bool EXT>
-static hipError_t launch_split(const GemmParams& p, int num_cu, hipStream_t s) {
-    const int64_t grid = tile4_grid<EPI>(p, num_cu);
+    const int64_t work = (tiles_m_max + p.E) * tiles_n;
+    const int64_t grid = work < num_cu ? work : num_cu;
     if (grid <= 0) return hipSuccess;
-    GemmParams q = p;
-    q.absorb_slots = static_cast<int>(grid);
-    q.stream_only = 1;
-    constexpr bool W_KN = false;
-    hipError_t err = launch_cfg<W_KN, EPI, EXT>(q, num_cu, s);
-    if (err != hipSuccess) return err;
-    q.stream_only = 0;
-    hipLaunchKernelGGL((tile4_kernel<EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, s, q);
+    hipLaunchKernelGGL((tile4_kernel<EPI, EXT>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
-// With a fragment-ordered weight copy (p.wfrag), the streaming items run as
-// one launch and the 256-row tiles as a second, four-wave launch.
+// With a fragment-ordered weight copy (p.wfrag) the whole GEMM is one
+// four-wave launch; otherwise one eight-wave launch.
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s) {
     const bool plain = plain_swiglu(p);
     if (!p.wfrag)
         return plain ? launch_cfg<false, EPI_SWIGLU, false>(p, num_cu, s)
                      : launch_cfg<false, EPI_SWIGLU, true>(p, num_cu, s);
-    return plain ? launch_split<EPI_SWIGLU, false>(p, num_cu, s) : launch_split<EPI_SWIGLU, true>(p, num_cu, s);
+    return plain ? launch_tile4<EPI_SWIGLU, false>(p, num_cu, s) : launch_tile4<EPI_SWIGLU, true>(p, num_cu, s);
 }
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag) return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
-    return launch_split<EPI_STORE, false>(p, num_cu, s);
+    return launch_tile4<EPI_STORE, false>(p, num_cu, s);
 }
 hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s) {
     const int64_t chunks = static_cast<int64_t>(E) * 5 * H * F / 8;
@@ -1593,18 +1728,7 @@ hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
 }
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag) return launch_cfg<true, EPI_STORE, false>(p, num_cu, s);
-    // the tiles read W1^T fragments (the same K-contiguous form as the forward
-    // copies); the streaming items read W1 transposed in the eight-wave kernel
-    const int64_t grid = tile4_grid<EPI_STORE>(p, num_cu);
-    if (grid <= 0) return hipSuccess;
-    GemmParams q = p;
-    q.absorb_slots = static_cast<int>(grid);
-    q.stream_only = 1;
-    hipError_t err = launch_cfg<true, EPI_STORE, false>(q, num_cu, s);
-    if (err != hipSuccess) return err;
-    q.stream_only = 0;
-    hipLaunchKernelGGL((tile4_kernel<EPI_STORE, false>), dim3(static_cast<unsigned>(grid)), dim3(T4_THREADS), 0, s, q);
-    return hipGetLastError();
+    return launch_tile4<EPI_STORE, false>(p, num_cu, s);   // W1^T fragments: the same K-contiguous form
 }
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
                             hipStream_t s) {
