@@ -105,6 +105,8 @@ def test_tiny_workload():
     # the maximum expert count with fragment copies: the four-wave tiles find
     # their expert among 1024 beside the streaming launch
     ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 256, 128),
+    # only thin items in the four-wave kernel: small experts at a shape with fragment copies
+    ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33, 96, 1], 512, 256),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
       0, 26, 22, 19, 27, 25, 31, 16, 24, 0, 21, 28, 23, 26, 18, 29, 22, 25, 20, 24], 264, 328),
