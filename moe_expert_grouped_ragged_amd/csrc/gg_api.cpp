@@ -332,6 +332,10 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
         r.N = static_cast<int>(2 * F);
         r.ldw = static_cast<int>(H);
         r.out0 = static_cast<uint16_t*>(workspace);
+        if (has_frag(H, F)) {   // the four-wave kernel over W1's fragment copy, columns put back in H1 order
+            r.wfrag = static_cast<const uint16_t*>(packed) + 3 * F * H;
+            r.h1_order = 1;
+        }
         if (gg::launch_fc2(r, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
     }
     // dA = dY W2_e, then the activation derivative with H1 -> dH1 (workspace;

@@ -35,6 +35,7 @@ struct GemmParams {
     // FC1, FC2 and dX: this GEMM's matrix in the fragment-ordered copy (same
     // expert stride), or null.  With it, the GEMM runs in the four-wave kernel.
     const uint16_t* wfrag;
+    int h1_order;              // plain store over W1's fragment copy: write the columns in H1's gate | up order
 };
 
 hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);

@@ -1230,6 +1230,13 @@ __device__ __forceinline__ void wfrag_load(bf16x8& w, const uint16_t* ptr) {
 __device__ __forceinline__ void wfrag_wait38(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
     asm volatile("s_waitcnt vmcnt(38)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
 }
+// H1 = X W1^T over the fragment-ordered W1 (plain-store variant): the copy's
+// 32-row block b holds W1 rows gate/up of 32 features (gate, gate, up, up per
+// 64 features), so its outputs go to H1 column h1_col(b, F) onwards.
+__device__ __forceinline__ int h1_col(int b, int F) {
+    return ((b & 3) < 2 ? 0 : F) + (b >> 2) * 64 + (b & 1) * 32;
+}
+__device__ __forceinline__ int F_of(int N) { return N >> 1; }   // N = 2F for the H1 GEMM
 // The same for a thin item's step (two weight blocks, 19 later loads).
 __device__ __forceinline__ void wfrag_wait19(bf16x8& a, bf16x8& b) {
     asm volatile("s_waitcnt vmcnt(19)" : "+v"(a), "+v"(b) :: "memory");
@@ -1376,8 +1383,9 @@ void tile4_kernel(const GemmParams p) {
                 const int idx = sidx * 64 + lane;
                 const int r = idx >> 3, c = idx & 7;
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (r & 7)) << 3));
+                const int oc = p.h1_order ? h1_col(tb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
                 if (r < rows)
-                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + gcol0 + c * 8) = v;
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
             }
         } else {
             // [96 rows][32 features] bf16 arrays for A, gate and up; 16-byte
@@ -1535,8 +1543,9 @@ void tile4_kernel(const GemmParams p) {
                 const int idx = sidx * 64 + lane;
                 const int r = idx >> 4, c = idx & 15;
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + ((c ^ (r & 15)) << 3));
+                const int oc = p.h1_order ? h1_col(rbw + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
                 if (wrow0 + r < row_end)
-                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(wrow0 + r) * N + gcol0 + c * 8) = v;
+                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(wrow0 + r) * N + oc) = v;
             }
         } else {
             // per pass of 64 token rows, [64][64] bf16 arrays for A, gate and up;
