@@ -2,14 +2,29 @@
 plus the input gradient) on one MI355X.
 
 One step = gg_forward_fc1_swiglu (saving H1) + gg_forward_fc2 + gg_dgrad
-over one synthetic batch that is already resident in HBM.  Prints ONE JSON
-line: grouped-GEMM TFLOP/s (12*M*H*F per step), routed rows/s, tokens/s,
-the roofline record of the dominant kernel (MFMA-bound FC1 grouped GEMM,
-timed with HIP events on the launch stream) and the CPU oracle timed on a
-bounded sample of the same workload.
+over one synthetic batch that is already resident in HBM.  Before every step
+(warm-up and timed) a 1 GiB scratch buffer is written, outside the timed
+events, so that no operand is left in the 256 MiB MALL or the L2 from the step
+before.  Each call is timed with HIP events on the launch stream; the step
+time is the median over the timed steps (the minimum is reported beside it).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+Prints ONE JSON line: grouped-GEMM TFLOP/s (12*M*H*F per step), routed
+rows/s, tokens/s, the roofline record of the dominant kernel (the FC1 grouped
+GEMM), the device, its clocks and the ROCm version, the parity of the run's
+GPU outputs against the CPU oracle on a sample of rows, and the CPU oracle
+timed on that sample.  The default workload is the largest one that fits one
+GPU: 128 experts, 32768 tokens x top-8 (each expert's rows padded up to a
+multiple of 256), hidden 4096, FFN 2048.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layout auto|frag|packed]
                     [--activation swiglu|qgeglu] [--weighted] [--recompute]
+
+Weights: the packed buffer alone (6*E*H*F bytes, the library's default) and,
+for shapes with H % 256 == 0 and F % 128 == 0, also with the opt-in
+fragment-ordered copies (gg_pack_frag, 10*E*H*F more bytes), which the
+extended calls take to run FC1, FC2 and dX in the four-wave kernel.  With
+--layout auto both are timed, the same steps each; the line's headline is
+the copies' arm (the faster), and "layouts" gives both.
 
 --activation / --weighted time the QuickGeGLU and router-probability-weighted
 variants (gg_forward_fc1_glu + gg_forward_fc2 + gg_dgrad_glu, dprobs
@@ -33,7 +48,8 @@ if ROOT not in sys.path:
 METRIC = "grouped-GEMM TFLOP/s + routed tokens/s (fwd+dgrad), % of MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-DEFAULT_WORKLOAD = "uniform_e32_h2048_f768"
+DEFAULT_WORKLOAD = "padded_e128_h4096_f2048"
+FLUSH_BYTES = 1 << 30          # > MALL (256 MiB) + all L2s: written before every step
 KERNEL_SOURCES = ["moe_expert_grouped_ragged_amd/csrc/gg_kernels.hip",
                   "moe_expert_grouped_ragged_amd/csrc/gg_kernels.h",
                   "moe_expert_grouped_ragged_amd/csrc/gg_api.cpp"]   # which kernels a call launches
@@ -87,6 +103,8 @@ def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
     off = case.offsets
     live = [e for e in range(case.E) if off[e + 1] > off[e]]
 
+    result = {}
+
     def run(k):
         rows = np.concatenate([np.arange(off[e], min(off[e] + k, off[e + 1])) for e in live]).astype(np.int64)
         _, comp = oracle.sample_rows(off, rows)
@@ -95,12 +113,14 @@ def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
         t0 = time.perf_counter()
         if act == "swiglu" and probs is None:
             fw = oracle.forward(xs, comp, w1, w2)
-            oracle.dgrad(dys, fw["h1"], comp, w1, w2)
+            dg = oracle.dgrad(dys, fw["h1"], comp, w1, w2)
         else:
             pr = None if probs is None else probs[rows]
             fw = oracle.forward_glu(xs, comp, w1, w2, act, pr)
-            oracle.dgrad_glu(dys, fw["h1"], comp, w1, w2, act, pr)
-        return rows.size, time.perf_counter() - t0
+            dg = oracle.dgrad_glu(dys, fw["h1"], comp, w1, w2, act, pr)
+        t = time.perf_counter() - t0
+        result.update(rows=rows, y=fw["y"], dx=dg["dx"])
+        return rows.size, t
 
     # grow the sample until one run takes about target_s (small samples
     # under-use the threads, so a single extrapolation undershoots)
@@ -112,10 +132,55 @@ def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
             break
         k = min(cap, max(k + 1, int(k * min(8.0, 0.9 * target_s / max(t, 1e-3)))))
     flops = 12.0 * n * case.H * case.F
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {k} rows of each of the {len(live)} non-empty experts ({n} routed rows "
-                      f"of {case.M}), forward + dgrad, {t:.1f} s",
-            "rows_per_s": n / t, "seconds": t}
+    rec = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {k} rows of each of the {len(live)} non-empty experts ({n} routed rows "
+                     f"of {case.M}), forward + dgrad, {t:.1f} s",
+           "rows_per_s": n / t, "seconds": t}
+    return rec, result
+
+
+def parity_of_sample(sample, y_gpu, dx_gpu):
+    """End-to-end parity of the run's GPU outputs on the oracle's sample rows:
+    Y from X and dX from dY (each side from its own forward), per element
+    against |d| <= 1e-2 |ref| + 1e-3 and in relative L2, in float64."""
+    import numpy as np
+    import torch
+    rows = torch.from_numpy(sample["rows"])
+    out = {}
+    for name, got, ref in (("y", y_gpu, sample["y"]), ("dx", dx_gpu, sample["dx"])):
+        g = got[rows.to(got.device)].float().cpu().numpy().astype(np.float64)
+        r = np.asarray(ref, np.float64)
+        d = np.abs(g - r)
+        ratio = d / (1e-2 * np.abs(r) + 1e-3)
+        out[name] = {"rel_l2": float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)),
+                     "worst_ratio": float(ratio.max()), "over_bound": int((ratio > 1.0).sum()),
+                     "elements": int(r.size), "exact_frac": float(np.mean(d == 0))}
+    out["rows"] = int(rows.numel())
+    out["bar"] = "rel_l2 <= 2e-3 and |d| <= 1e-2|ref| + 1e-3 per element"
+    return out
+
+
+def device_record(dev):
+    """Device name, architecture, clocks (rocm-smi, if it answers) and the
+    ROCm / HIP versions."""
+    import subprocess
+
+    import torch
+    prop = torch.cuda.get_device_properties(dev)
+    rec = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
+           "compute_units": prop.multi_processor_count, "hip_runtime": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rec["rocm"] = fh.read().strip()
+    except OSError:
+        rec["rocm"] = None
+    try:
+        proc = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(proc.stdout).values()))
+        rec["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))}
+    except Exception as exc:   # a missing or silent rocm-smi must not fail the benchmark
+        rec["clocks"] = f"unavailable ({type(exc).__name__})"
+    return rec
 
 
 def launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args):
@@ -214,6 +279,10 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="forward without saving H1 and input gradient through gg_dgrad_recompute "
                          "(FC1 recomputed from X inside the dgrad call)")
+    ap.add_argument("--layout", choices=("auto", "frag", "packed"), default="auto",
+                    help="weights: 'packed' = the packed buffer alone (the library's default); 'frag' = with "
+                         "the opt-in fragment-ordered copies (gg_pack_frag); 'auto' = both where the shape "
+                         "has copies, the line's headline being 'frag'")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -249,6 +318,17 @@ def main():
     x, dy = case.x.to(dev), case.dy.to(dev)
     off = torch.from_numpy(case.offsets).to(dev)
     packed = gg.gg_pack_weights(case.w1.to(dev), case.w2.to(dev))
+    # weight layouts timed: the packed buffer alone (the default), and with the
+    # opt-in fragment-ordered copies where the shape has them; the headline is
+    # the first of them
+    if args.layout == "auto":
+        arms = ["frag", "packed"] if gg.has_frag(H, F) else ["packed"]
+    else:
+        arms = [args.layout]
+    if "frag" in arms and not gg.has_frag(H, F):
+        print(f"bench.py: H={H}, F={F} has no fragment-ordered copies", file=sys.stderr)
+        sys.exit(2)
+    frag = gg.gg_pack_frag(packed, E, H, F) if "frag" in arms else None
     h1 = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     a = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
     y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
@@ -259,40 +339,41 @@ def main():
                 if args.weighted else None)
     probs = torch.from_numpy(probs_np).to(dev) if args.weighted else None
     dprobs = torch.empty(M, dtype=torch.float32, device=dev) if args.weighted else None
-    ws_glu = (torch.empty(gg.dgrad_glu_workspace_bytes(M, F, args.weighted), dtype=torch.uint8, device=dev)
-              if glu else None)
+    ws_glu = torch.empty(gg.dgrad_glu_workspace_bytes(M, F, args.weighted), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    ev = {k: [] for k in ("fc1", "fc2", "dgrad")}
-
-    def step(record):
-        if record:
+    def step(arm, ev):
+        fr = frag if arm == "frag" else None
+        if ev is not None:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e2 = torch.cuda.Event(enable_timing=True)
             e3 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         if args.recompute:
-            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, save_h1=False, a_out=a)
-        elif glu:
-            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a)
+            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, save_h1=False, a_out=a, frag=fr)
+        elif glu or fr is not None:
+            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a, frag=fr)
         else:
             gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
-        if record:
+        if ev is not None:
             e1.record(stream)
-        gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
-        if record:
+        if fr is None:
+            gg.gg_forward_fc2(a, off, packed, E, H, F, y=y)
+        else:
+            gg.gg_forward_fc2_frag(a, off, packed, fr, E, H, F, y=y)
+        if ev is not None:
             e2.record(stream)
         if args.recompute:
             gg.gg_dgrad_recompute(dy, x, off, packed, E, H, F, args.activation, probs,
-                                  want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs)
-        elif glu:
+                                  want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs, frag=fr)
+        elif glu or fr is not None:
             gg.gg_dgrad_glu(dy, h1, off, packed, E, H, F, args.activation, probs,
-                            want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs)
+                            want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs, frag=fr)
         else:
             gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
-        if record:
+        if ev is not None:
             e3.record(stream)
             ev["fc1"].append((e0, e1))
             ev["fc2"].append((e1, e2))
@@ -302,33 +383,54 @@ def main():
         print(json.dumps(launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args)), flush=True)
         return
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    call_ms = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in ev.items()}
+    # a scratch buffer larger than the MALL and all L2s, written before every
+    # step outside the timed events, so that each step starts cold
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def evict(i):
+        flush.fill_(i & 0xFF)
+
+    def timed_arm(arm):
+        ev = {k: [] for k in ("fc1", "fc2", "dgrad")}
+        for i in range(args.warmup):
+            evict(i)
+            step(arm, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            evict(i)
+            step(arm, ev)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps          # includes the evictions
+        per_step = {k: np.array([s.elapsed_time(e) for s, e in v]) for k, v in ev.items()}
+        steps_ms = per_step["fc1"] + per_step["fc2"] + per_step["dgrad"]
+        return {"ms_per_step": float(np.median(steps_ms)), "ms_per_step_min": float(np.min(steps_ms)),
+                "wall_ms_per_step_incl_eviction": wall_ms,
+                "per_call_ms": {k: float(np.median(v)) for k, v in per_step.items()},
+                "per_call_min_ms": {k: float(np.min(v)) for k, v in per_step.items()}}
+
+    # the headline arm last, so that the outputs left in y and dx are its own
+    results = {arm: timed_arm(arm) for arm in reversed(arms)}
+    head = results[arms[0]]
+    ms, wall_ms = head["ms_per_step"], head["wall_ms_per_step_incl_eviction"]
+    call_ms, call_min_ms = head["per_call_ms"], head["per_call_min_ms"]
+    steps_min = head["ms_per_step_min"]
 
     flops = workload.flops_fwd_dgrad(M, H, F)
     tflops = flops / (ms * 1e-3) / 1e12
     n_live = int(np.count_nonzero(np.diff(case.offsets)))
     bfwd, bdg = algorithmic_bytes(M, H, F, n_live)
     # dominant kernel: the FC1 grouped GEMM with the SwiGLU epilogue (the
-    # largest share of the step), one launch per gg_forward_fc1_swiglu call:
-    # the four-wave kernel when the packed buffer holds fragment-ordered
-    # weights (H % 256 == 0 and F % 128 == 0), else the eight-wave kernel.
+    # largest share of the step), one launch per FC1 call: the four-wave
+    # kernel with the fragment-ordered weight copies, else the eight-wave
+    # kernel.
     # Algorithmic work per launch: 4*M*H*F FLOPs; HBM bytes = X read (2MH) +
     # W1 of the experts with rows (4HF each) + H1 and A written (4MF + 2MF).
     # The bound is whichever of MFMA time and HBM time is larger.
     fc1_flops = 4.0 * M * H * F
     fc1_bytes = 2.0 * M * H + 4.0 * H * F * n_live + 6.0 * M * F
     fc1_ms = call_ms["fc1"]
-    four = H % 256 == 0 and F % 128 == 0
-    kname = "tile4_kernel<SwiGLU>" if four else "grouped_gemm_kernel<FC1+SwiGLU>"
+    kname = "tile4_kernel<SwiGLU>" if arms[0] == "frag" else "grouped_gemm_kernel<FC1+SwiGLU>"
     mfma_bound = fc1_flops / (PEAK_BF16_TFLOPS * 1e12) >= fc1_bytes / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
@@ -338,29 +440,43 @@ def main():
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
         roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
-    roof.update({"traffic": None if glu else load_traffic(args.workload, "fc1"), "avg_launch_ms": fc1_ms,
+    roof.update({"traffic": None if glu else load_traffic(args.workload, f"fc1_{arms[0]}"),
+                 "median_launch_ms": fc1_ms, "min_launch_ms": call_min_ms["fc1"],
                  "flops_per_launch": fc1_flops, "algorithmic_bytes_per_launch": fc1_bytes})
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "experts": E, "tokens": case.T, "topk": w.topk,
-                   "routed_rows": M, "hidden": H, "ffn": F, "routing": w.routing,
+                   "routed_rows": M, "real_rows": int(case.counts.sum()), "hidden": H, "ffn": F,
+                   "routing": w.routing, "pad_to": w.pad_to,
                    "parallelism": "single-gpu", "activation": args.activation,
-                   "weighted": bool(args.weighted), "recompute_fc1_in_dgrad": bool(args.recompute)},
+                   "weighted": bool(args.weighted), "recompute_fc1_in_dgrad": bool(args.recompute),
+                   "weights": ("packed buffer (6*E*H*F bytes) + opt-in fragment-ordered copies (10*E*H*F bytes)"
+                               if arms[0] == "frag" else "packed buffer (6*E*H*F bytes)")},
+        "timing": "median over the timed steps of HIP-event step times on the launch stream; a 1 GiB "
+                  "scratch write before every step (outside the events) evicts the MALL and L2",
+        "ms_per_step_min": steps_min,
+        "wall_ms_per_step_incl_eviction": wall_ms,
         "routed_rows_per_s": M / (ms * 1e-3), "tokens_per_s": case.T / (ms * 1e-3),
+        "real_rows_tflops": 12.0 * int(case.counts.sum()) * H * F / (ms * 1e-3) / 1e12,
         "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "hbm_GBps_algorithmic": (bfwd + bdg) / (ms * 1e-3) / 1e9,
         "hbm_frac": (bfwd + bdg) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_call_ms": call_ms,
+        "per_call_min_ms": call_min_ms,
+        "layouts": {arm: dict(r, tflops=flops / (r["ms_per_step"] * 1e-3) / 1e12) for arm, r in results.items()},
         "roofline": roof,
         "kernel_source_sha": kernel_source_hash(),
-        "device": torch.cuda.get_device_name(dev),
+        "device": device_record(dev),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, args.activation, probs_np)
+        rec, sample = cpu_baseline(case, args.cpu_seconds, args.activation, probs_np)
+        out["cpu_baseline"] = rec
+        out["parity"] = parity_of_sample(sample, y, dx)
     else:
         out["cpu_baseline"] = None
+        out["parity"] = None
     print(json.dumps(out), flush=True)
 
 

@@ -75,30 +75,53 @@ typedef enum {
 /* Human-readable name of a status code (static string). */
 const char* gg_status_string(int status);
 
-/* Bytes of the packed weight buffer.  Expert-major blocks: expert e's block
- * holds W1_e [2F][H] then W2_e [H][F], bf16 row-major.  When H % 256 == 0 and
- * F % 128 == 0 the block also holds, after them, copies of W1_e, W2_e and
- * W1_e^T in MFMA fragment order (read by the forward tiles and by the dX
- * GEMM; written by gg_pack_weights): 16*E*H*F bytes in all, 6*E*H*F
- * otherwise.  One expert block is itself a packed buffer with E = 1. */
+/* Bytes of the packed weight buffer: 6*E*H*F.  Expert-major blocks of 3*F*H
+ * bf16 elements: W1_e [2F][H] at element offset e*3*F*H, then W2_e [H][F]
+ * at e*3*F*H + 2*F*H, both row-major.  One expert block (or any contiguous
+ * range of them) is itself a packed buffer with E = 1 (or the range's E).
+ * Returns 0 when E, H or F is not positive. */
 size_t gg_packed_bytes(int64_t E, int64_t H, int64_t F);
 
 /* Bytes of the gg_dgrad workspace: dH1 [M][2F] bf16 = 4*M*F. */
 size_t gg_dgrad_workspace_bytes(int64_t M, int64_t F);
 
-/* Pack E experts' frozen weights into `packed` (expert-major layout above).
+/* Pack E experts' frozen weights into `packed` (expert-major layout above),
+ * so that every expert's parameters can become views into one contiguous
+ * buffer, as the runtime packing of frozen expert weights does in the first
+ * page ("Artifacts" and "Why existing behavior remains safe", which also note
+ * an unchanged peak allocated memory: the buffer is exactly the weights).
  * w1, w2: HOST arrays of E DEVICE pointers; w1[e] -> [2F][H], w2[e] -> [H][F].
  * A source that already is its destination inside `packed` is skipped, so
  * re-packing after one expert's weights were replaced copies only what
- * moved (recovery after a middle expert weight is replaced, "Why existing
- * behavior remains safe").  A source that partially overlaps `packed` gives
- * GG_ERR_ALIASING.  Copies are asynchronous device-to-device on `stream`.
- * The fragment-ordered copies (see gg_packed_bytes) are always rewritten, so
- * after writing weights straight into the packed buffer, call this again
- * with those locations as sources. */
+ * moved (recovery after a middle expert weight is replaced, same section).
+ * A source that partially overlaps `packed` gives GG_ERR_ALIASING.  Copies
+ * are asynchronous device-to-device on `stream`.  packed_bytes is the size
+ * of `packed` (at least gg_packed_bytes(E, H, F)). */
 int gg_pack_weights(int64_t E, int64_t H, int64_t F,
                     const void* const* w1, const void* const* w2,
                     void* packed, size_t packed_bytes, hipStream_t stream);
+
+/* ---- Opt-in fragment-ordered weight copies (this library's own layout;
+ * the pages pack only the original matrices).  For shapes with H % 256 == 0
+ * and F % 128 == 0, a second, caller-owned buffer can hold copies of every
+ * expert's W1, W2 and W1^T in the operand order of the CDNA4 bf16 matrix
+ * instruction, which lets FC1, FC2 and the dX GEMM load their weight operands
+ * straight into registers.  The extended calls below take it as `frag`
+ * (NULL: not used).  It costs 10*E*H*F more bytes (5/3 of the weights) and
+ * buys about 8-12% on those GEMMs.  The copies are derived from the packed
+ * buffer by gg_pack_frag and do not follow later writes to it: call
+ * gg_pack_frag again after re-packing. */
+
+/* Bytes of the fragment buffer: 10*E*H*F when H % 256 == 0 and F % 128 == 0,
+ * 0 for every other shape (no copies exist for it). */
+size_t gg_frag_bytes(int64_t E, int64_t H, int64_t F);
+
+/* Write the fragment-ordered copies of the E experts of `packed` into
+ * `frag` (DEVICE, 16-byte aligned, frag_bytes >= gg_frag_bytes(E, H, F)).
+ * Asynchronous on `stream`.  GG_ERR_INVALID_ARGUMENT for a shape without
+ * copies; GG_ERR_ALIASING if the buffers overlap. */
+int gg_pack_frag(int64_t E, int64_t H, int64_t F, const void* packed, size_t packed_bytes,
+                 void* frag, size_t frag_bytes, hipStream_t stream);
 
 /* Forward FC1 with the fused SwiGLU epilogue.
  * x [M][H]; packed as above; h1_out [M][2F] (the bf16 FC1 output, saved for
@@ -145,13 +168,22 @@ size_t gg_dgrad_glu_workspace_bytes(int64_t M, int64_t F, int with_dprobs);
 
 /* gg_forward_fc1_swiglu with the activation chosen by `activation` (a
  * gg_activation) and, when `probs` is not NULL, each routed row's activation
- * scaled by probs[r] (DEVICE fp32 [M], 4-byte aligned, read only).  An
- * unknown activation gives GG_ERR_INVALID_ARGUMENT.  With GG_ACT_SWIGLU and
- * probs == NULL the results are those of gg_forward_fc1_swiglu, bit for bit. */
+ * scaled by probs[r] (DEVICE fp32 [M], 4-byte aligned, read only).  `frag`
+ * is NULL or the fragment buffer of the same weights (gg_pack_frag); the
+ * results do not depend on it, bit for bit.  An unknown activation, or a
+ * frag for a shape without copies, gives GG_ERR_INVALID_ARGUMENT.  With
+ * GG_ACT_SWIGLU and probs == NULL the results are those of
+ * gg_forward_fc1_swiglu, bit for bit. */
 int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M,
-                       const void* packed, int64_t E, int64_t H, int64_t F,
+                       const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
                        int activation, const float* probs,
                        void* h1_out, void* a_out, hipStream_t stream);
+
+/* gg_forward_fc2 with an optional fragment buffer (`frag` as in
+ * gg_forward_fc1_glu); the results are those of gg_forward_fc2, bit for bit. */
+int gg_forward_fc2_frag(const void* a, const int64_t* offsets, int64_t M,
+                        const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
+                        void* y, hipStream_t stream);
 
 /* Input gradient of gg_forward_fc1_glu + gg_forward_fc2: as gg_dgrad, with
  * the same `activation` and `probs` as the forward.  dprobs (DEVICE fp32 [M],
@@ -159,9 +191,10 @@ int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M,
  * must then hold gg_dgrad_glu_workspace_bytes(M, F, 1) bytes (dH1 first, then
  * the partial sums).  Two launches on `stream`, three with dprobs.  With
  * GG_ACT_SWIGLU, probs == NULL and dprobs == NULL the results are those of
- * gg_dgrad, bit for bit. */
+ * gg_dgrad, bit for bit.  `frag` as in gg_forward_fc1_glu (used by the dX
+ * GEMM; the results do not depend on it). */
 int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
-                 const void* packed, int64_t E, int64_t H, int64_t F,
+                 const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
                  int activation, const float* probs,
                  void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
                  hipStream_t stream);
@@ -181,7 +214,7 @@ int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t
  * dprobs equal those of gg_dgrad_glu with the saved H1, bit for bit.
  * Other arguments as gg_dgrad_glu. */
 int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, int64_t M,
-                       const void* packed, int64_t E, int64_t H, int64_t F,
+                       const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
                        int activation, const float* probs,
                        void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
                        hipStream_t stream);

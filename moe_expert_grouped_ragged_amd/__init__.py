@@ -12,6 +12,11 @@ current stream.  The functions carry the C names:
   gg_dgrad_glu(dy, h1, offsets, packed, ..., activation, probs)  -> (dx, dprobs)
   gg_dgrad_recompute(dy, x, offsets, packed, ...)                 -> (dx, dprobs)
         (no saved H1: FC1 is recomputed from x inside the call)
+  gg_pack_frag(packed, E, H, F)                  -> opt-in fragment buffer
+  gg_forward_fc2_frag(a, offsets, packed, frag, ...) -> y
+        (the *_glu, recompute and fc2_frag calls take `frag`: fragment-ordered
+        weight copies that speed up FC1, FC2 and dX for H % 256 == 0 and
+        F % 128 == 0, at 10*E*H*F more bytes)
 
 The *_glu calls add the QuickGeGLU activation and the weighting of the
 activation by each row's router probability (fp32 [M]), with dp of that
@@ -50,7 +55,8 @@ ACTIVATIONS = {"swiglu": GG_ACT_SWIGLU, "qgeglu": GG_ACT_QGEGLU}
 
 EXPORTED = ("gg_status_string", "gg_packed_bytes", "gg_dgrad_workspace_bytes", "gg_pack_weights",
             "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16",
-            "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute")
+            "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute",
+            "gg_frag_bytes", "gg_pack_frag", "gg_forward_fc2_frag")
 
 
 def _load() -> ctypes.CDLL:
@@ -63,20 +69,25 @@ def _load() -> ctypes.CDLL:
     lib.gg_status_string.restype = ctypes.c_char_p
     lib.gg_packed_bytes.argtypes = [i64, i64, i64]
     lib.gg_packed_bytes.restype = sz
+    lib.gg_frag_bytes.argtypes = [i64, i64, i64]
+    lib.gg_frag_bytes.restype = sz
     lib.gg_dgrad_workspace_bytes.argtypes = [i64, i64]
     lib.gg_dgrad_workspace_bytes.restype = sz
     lib.gg_pack_weights.argtypes = [i64, i64, i64, ctypes.POINTER(p), ctypes.POINTER(p), p, sz, p]
+    lib.gg_pack_frag.argtypes = [i64, i64, i64, p, sz, p, sz, p]
     lib.gg_forward_fc1_swiglu.argtypes = [p, p, i64, p, i64, i64, i64, p, p, p]
     lib.gg_forward_fc2.argtypes = [p, p, i64, p, i64, i64, i64, p, p]
+    lib.gg_forward_fc2_frag.argtypes = [p, p, i64, p, p, i64, i64, i64, p, p]
     lib.gg_dgrad.argtypes = [p, p, p, i64, p, i64, i64, i64, p, sz, p, p]
     lib.gg_round_bf16.argtypes = [p, p, i64, p]
     lib.gg_dgrad_glu_workspace_bytes.argtypes = [i64, i64, i32]
     lib.gg_dgrad_glu_workspace_bytes.restype = sz
-    lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, i64, i64, i64, i32, p, p, p, p]
-    lib.gg_dgrad_glu.argtypes = [p, p, p, i64, p, i64, i64, i64, i32, p, p, sz, p, p, p]
-    lib.gg_dgrad_recompute.argtypes = [p, p, p, i64, p, i64, i64, i64, i32, p, p, sz, p, p, p]
-    for name in ("gg_pack_weights", "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad",
-                 "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute"):
+    lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, p, i64, i64, i64, i32, p, p, p, p]
+    lib.gg_dgrad_glu.argtypes = [p, p, p, i64, p, p, i64, i64, i64, i32, p, p, sz, p, p, p]
+    lib.gg_dgrad_recompute.argtypes = [p, p, p, i64, p, p, i64, i64, i64, i32, p, p, sz, p, p, p]
+    for name in ("gg_pack_weights", "gg_pack_frag", "gg_forward_fc1_swiglu", "gg_forward_fc2",
+                 "gg_forward_fc2_frag", "gg_dgrad", "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu",
+                 "gg_dgrad_recompute"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -104,24 +115,81 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _bf16_cuda(t: torch.Tensor, name: str) -> torch.Tensor:
+def _bf16_cuda(t: torch.Tensor, name: str, shape=None, device=None) -> torch.Tensor:
+    """A contiguous bf16 device tensor (of the given shape, on the given device)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if t.dtype != torch.bfloat16:
         raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     return t
 
 
-def _offsets(offsets: torch.Tensor, E: int) -> torch.Tensor:
-    if offsets.dtype != torch.int64 or not offsets.is_cuda or offsets.shape != (E + 1,):
-        raise ValueError("offsets must be an int64 device tensor of shape [E+1]")
+def _offsets(offsets: torch.Tensor, E: int, device) -> torch.Tensor:
+    if (not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.int64 or not offsets.is_cuda
+            or offsets.shape != (E + 1,) or offsets.device != device):
+        raise ValueError(f"offsets must be an int64 tensor of shape [E+1] on {device}")
     return offsets.contiguous()
+
+
+def _packed(packed: torch.Tensor, E: int, H: int, F: int, device) -> torch.Tensor:
+    """The packed weights: a contiguous bf16 buffer of at least packed_bytes(E, H, F)."""
+    _bf16_cuda(packed, "packed", device=device)
+    need = packed_bytes(E, H, F)
+    if need == 0 or packed.numel() * 2 < need:
+        raise ValueError(f"packed holds {packed.numel() * 2} bytes; E={E}, H={H}, F={F} needs {need}")
+    return packed
+
+
+def _frag(frag: Optional[torch.Tensor], E: int, H: int, F: int, device) -> Optional[torch.Tensor]:
+    """An optional fragment buffer of at least frag_bytes(E, H, F)."""
+    if frag is None:
+        return None
+    _bf16_cuda(frag, "frag", device=device)
+    need = frag_bytes(E, H, F)
+    if need == 0:
+        raise ValueError(f"H={H}, F={F} has no fragment-ordered copies (needs H % 256 == 0 and F % 128 == 0)")
+    if frag.numel() * 2 < need:
+        raise ValueError(f"frag holds {frag.numel() * 2} bytes; E={E}, H={H}, F={F} needs {need}")
+    return frag
+
+
+def _out(t: Optional[torch.Tensor], shape, name: str, device) -> torch.Tensor:
+    """A caller-given output (checked) or a new one."""
+    if t is None:
+        return torch.empty(*shape, dtype=torch.bfloat16, device=device)
+    return _bf16_cuda(t, name, shape=shape, device=device)
+
+
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    """A caller-given workspace (contiguous, on the device, any dtype, >= nbytes) or a new one."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {nbytes} needed")
+    return ws
 
 
 def packed_bytes(E: int, H: int, F: int) -> int:
     return int(lib.gg_packed_bytes(E, H, F))
+
+
+def frag_bytes(E: int, H: int, F: int) -> int:
+    """Bytes of the opt-in fragment-ordered copies (0 when the shape has none)."""
+    return int(lib.gg_frag_bytes(E, H, F))
+
+
+def has_frag(H: int, F: int) -> bool:
+    return frag_bytes(1, H, F) > 0
 
 
 def dgrad_workspace_bytes(M: int, F: int) -> int:
@@ -133,9 +201,9 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
                     packed: Optional[torch.Tensor] = None,
                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Pack frozen expert weights (w1[e]: [2F, H], gate rows then up rows;
-    w2[e]: [H, F]) into one expert-major bf16 buffer.  Returns the packed
-    buffer (1-D, packed_bytes(E, H, F) / 2 elements).  Per-expert views into it:
-    ``expert_views(packed, E, H, F)``."""
+    w2[e]: [H, F]) into one expert-major bf16 buffer of exactly the weights'
+    size.  Returns the packed buffer (1-D, packed_bytes(E, H, F) / 2
+    elements).  Per-expert views into it: ``expert_views(packed, E, H, F)``."""
     w1s = list(w1.unbind(0)) if isinstance(w1, torch.Tensor) else list(w1)
     w2s = list(w2.unbind(0)) if isinstance(w2, torch.Tensor) else list(w2)
     if len(w1s) != len(w2s) or not w1s:
@@ -148,6 +216,8 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
             raise ValueError("expert base weights must be frozen (requires_grad=False)")
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("expert weights must be contiguous device tensors")
+        if t.device != w1s[0].device:
+            raise ValueError("expert weights must all be on one device")
     E = len(w1s)
     twoF, H = w1s[0].shape
     F = twoF // 2
@@ -156,6 +226,7 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
     nbytes = packed_bytes(E, H, F)
     if packed is None:
         packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w1s[0].device)
+    _packed(packed, E, H, F, w1s[0].device)
     arr1 = (ctypes.c_void_p * E)(*[t.data_ptr() for t in w1s])
     arr2 = (ctypes.c_void_p * E)(*[t.data_ptr() for t in w2s])
     _check(lib.gg_pack_weights(E, H, F, arr1, arr2, packed.data_ptr(), packed.numel() * 2,
@@ -163,10 +234,27 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
     return packed
 
 
+def gg_pack_frag(packed: torch.Tensor, E: int, H: int, F: int, frag: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Opt-in fragment-ordered copies of the packed weights (H % 256 == 0 and
+    F % 128 == 0 only): returns the fragment buffer (frag_bytes(E, H, F) / 2
+    bf16 elements) to pass as ``frag`` to the extended calls."""
+    _packed(packed, E, H, F, packed.device)
+    need = frag_bytes(E, H, F)
+    if need == 0:
+        raise ValueError(f"H={H}, F={F} has no fragment-ordered copies (needs H % 256 == 0 and F % 128 == 0)")
+    if frag is None:
+        frag = torch.empty(need // 2, dtype=torch.bfloat16, device=packed.device)
+    _frag(frag, E, H, F, packed.device)
+    _check(lib.gg_pack_frag(E, H, F, packed.data_ptr(), packed.numel() * 2, frag.data_ptr(), frag.numel() * 2,
+                            _stream_ptr(stream)), "gg_pack_frag")
+    return frag
+
+
 def expert_views(packed: torch.Tensor, E: int, H: int, F: int):
-    """(w1_views, w2_views): per-expert views into the packed buffer.  After
-    writing through them, call gg_pack_weights(w1_views, w2_views, packed=packed)
-    so that the derived fragment-ordered copies follow."""
+    """(w1_views, w2_views): per-expert views into the packed buffer.  A
+    fragment buffer derived from it does not follow writes through them: call
+    gg_pack_frag again."""
     per = packed_bytes(1, H, F) // 2
     w1 = [packed[e * per:e * per + 2 * F * H].view(2 * F, H) for e in range(E)]
     w2 = [packed[e * per + 2 * F * H:e * per + 3 * F * H].view(H, F) for e in range(E)]
@@ -180,15 +268,15 @@ def gg_forward_fc1_swiglu(x: torch.Tensor, offsets: torch.Tensor, packed: torch.
                           ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """FC1 (x [M, H] -> H1 [M, 2F]) with the fused SwiGLU -> A [M, F]."""
     _bf16_cuda(x, "x")
-    _bf16_cuda(packed, "packed")
-    M = x.shape[0]
-    if x.shape != (M, H):
-        raise ValueError("x must be [M, H]")
-    off = _offsets(offsets, E)
-    if a_out is None:
-        a_out = torch.empty(M, F, dtype=torch.bfloat16, device=x.device)
+    M, dev = x.shape[0], x.device
+    _bf16_cuda(x, "x", shape=(M, H))
+    _packed(packed, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    if h1_out is not None:
+        _bf16_cuda(h1_out, "h1_out", shape=(M, 2 * F), device=dev)
+    a_out = _out(a_out, (M, F), "a_out", dev)
     if h1_out is None and save_h1:
-        h1_out = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=x.device)
+        h1_out = _out(None, (M, 2 * F), "h1_out", dev)
     _check(lib.gg_forward_fc1_swiglu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
                                      _ptr(h1_out), a_out.data_ptr(), _stream_ptr(stream)),
            "gg_forward_fc1_swiglu")
@@ -199,16 +287,28 @@ def gg_forward_fc2(a: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
                    E: int, H: int, F: int, y: Optional[torch.Tensor] = None,
                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """FC2: a [M, F] -> y [M, H]."""
+    return gg_forward_fc2_frag(a, offsets, packed, None, E, H, F, y=y, stream=stream)
+
+
+def gg_forward_fc2_frag(a: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
+                        frag: Optional[torch.Tensor], E: int, H: int, F: int, y: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """FC2 with an optional fragment buffer (gg_pack_frag): a [M, F] -> y [M, H]."""
     _bf16_cuda(a, "a")
-    _bf16_cuda(packed, "packed")
-    M = a.shape[0]
-    if a.shape != (M, F):
-        raise ValueError("a must be [M, F]")
-    off = _offsets(offsets, E)
-    if y is None:
-        y = torch.empty(M, H, dtype=torch.bfloat16, device=a.device)
-    _check(lib.gg_forward_fc2(a.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
-                              y.data_ptr(), _stream_ptr(stream)), "gg_forward_fc2")
+    M, dev = a.shape[0], a.device
+    _bf16_cuda(a, "a", shape=(M, F))
+    _packed(packed, E, H, F, dev)
+    fr = _frag(frag, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    y = _out(y, (M, H), "y", dev)
+    if fr is None:
+        st = lib.gg_forward_fc2(a.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F, y.data_ptr(),
+                                _stream_ptr(stream))
+        _check(st, "gg_forward_fc2")
+    else:
+        st = lib.gg_forward_fc2_frag(a.data_ptr(), off.data_ptr(), M, packed.data_ptr(), fr.data_ptr(), E, H, F,
+                                     y.data_ptr(), _stream_ptr(stream))
+        _check(st, "gg_forward_fc2_frag")
     return y
 
 
@@ -217,18 +317,20 @@ def gg_dgrad(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: 
              dx: Optional[torch.Tensor] = None,
              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Input gradient: dy [M, H], saved h1 [M, 2F] -> dx [M, H].  The
-    workspace (bf16 [M, 2F] or larger) receives dH1."""
+    workspace (bf16 [M, 2F] or any buffer of dgrad_workspace_bytes) receives dH1."""
     _bf16_cuda(dy, "dy")
-    _bf16_cuda(h1, "h1")
-    _bf16_cuda(packed, "packed")
-    M = dy.shape[0]
-    if dy.shape != (M, H) or h1.shape != (M, 2 * F):
-        raise ValueError("dy must be [M, H] and h1 [M, 2F]")
-    off = _offsets(offsets, E)
-    if workspace is None:
-        workspace = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dy.device)
-    if dx is None:
-        dx = torch.empty(M, H, dtype=torch.bfloat16, device=dy.device)
+    M, dev = dy.shape[0], dy.device
+    _bf16_cuda(dy, "dy", shape=(M, H))
+    _bf16_cuda(h1, "h1", shape=(M, 2 * F), device=dev)
+    _packed(packed, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    if dx is not None:
+        _bf16_cuda(dx, "dx", shape=(M, H), device=dev)
+    if workspace is not None:
+        _workspace(workspace, dgrad_workspace_bytes(M, F), dev)
+    else:
+        workspace = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
+    dx = _out(dx, (M, H), "dx", dev)
     _check(lib.gg_dgrad(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                         dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad")
@@ -243,11 +345,12 @@ def _activation(activation) -> int:
     return int(activation)
 
 
-def _probs_cuda(probs: Optional[torch.Tensor], M: int, name: str = "probs") -> Optional[torch.Tensor]:
+def _probs_cuda(probs: Optional[torch.Tensor], M: int, device, name: str = "probs") -> Optional[torch.Tensor]:
     if probs is None:
         return None
-    if probs.dtype != torch.float32 or not probs.is_cuda or probs.shape != (M,) or not probs.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 device tensor of shape [M]")
+    if (probs.dtype != torch.float32 or not probs.is_cuda or probs.shape != (M,) or not probs.is_contiguous()
+            or probs.device != device):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape [M] on {device}")
     return probs
 
 
@@ -258,22 +361,25 @@ def dgrad_glu_workspace_bytes(M: int, F: int, with_dprobs: bool) -> int:
 def gg_forward_fc1_glu(x: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
                        E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
                        save_h1: bool = True, h1_out: Optional[torch.Tensor] = None,
-                       a_out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
+                       a_out: Optional[torch.Tensor] = None, frag: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None
                        ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """FC1 with the fused activation ("swiglu" | "qgeglu"), optionally scaled
-    per row by probs (float32 [M]) -> (H1 or None, A)."""
+    per row by probs (float32 [M]) -> (H1 or None, A).  frag: optional
+    fragment buffer (gg_pack_frag) of the same weights."""
     _bf16_cuda(x, "x")
-    _bf16_cuda(packed, "packed")
-    M = x.shape[0]
-    if x.shape != (M, H):
-        raise ValueError("x must be [M, H]")
-    off = _offsets(offsets, E)
-    pr = _probs_cuda(probs, M)
-    if a_out is None:
-        a_out = torch.empty(M, F, dtype=torch.bfloat16, device=x.device)
+    M, dev = x.shape[0], x.device
+    _bf16_cuda(x, "x", shape=(M, H))
+    _packed(packed, E, H, F, dev)
+    fr = _frag(frag, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    pr = _probs_cuda(probs, M, dev)
+    if h1_out is not None:
+        _bf16_cuda(h1_out, "h1_out", shape=(M, 2 * F), device=dev)
+    a_out = _out(a_out, (M, F), "a_out", dev)
     if h1_out is None and save_h1:
-        h1_out = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=x.device)
-    _check(lib.gg_forward_fc1_glu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+        h1_out = _out(None, (M, 2 * F), "h1_out", dev)
+    _check(lib.gg_forward_fc1_glu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr), E, H, F,
                                   _activation(activation), _ptr(pr), _ptr(h1_out), a_out.data_ptr(),
                                   _stream_ptr(stream)), "gg_forward_fc1_glu")
     return h1_out, a_out
@@ -283,28 +389,30 @@ def gg_dgrad_glu(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, pack
                  E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
                  want_dprobs: bool = True, workspace: Optional[torch.Tensor] = None,
                  dx: Optional[torch.Tensor] = None, dprobs: Optional[torch.Tensor] = None,
-                 stream: Optional[torch.cuda.Stream] = None
+                 frag: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Input gradient of gg_forward_fc1_glu + FC2 -> (dx, dprobs or None).
     The workspace (a byte buffer of dgrad_glu_workspace_bytes) keeps dH1 [M, 2F]
-    bf16 at its start."""
+    bf16 at its start.  frag: optional fragment buffer (gg_pack_frag)."""
     _bf16_cuda(dy, "dy")
-    _bf16_cuda(h1, "h1")
-    _bf16_cuda(packed, "packed")
-    M = dy.shape[0]
-    if dy.shape != (M, H) or h1.shape != (M, 2 * F):
-        raise ValueError("dy must be [M, H] and h1 [M, 2F]")
-    off = _offsets(offsets, E)
-    pr = _probs_cuda(probs, M)
+    M, dev = dy.shape[0], dy.device
+    _bf16_cuda(dy, "dy", shape=(M, H))
+    _bf16_cuda(h1, "h1", shape=(M, 2 * F), device=dev)
+    _packed(packed, E, H, F, dev)
+    fr = _frag(frag, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    pr = _probs_cuda(probs, M, dev)
+    dprobs = _probs_cuda(dprobs, M, dev, "dprobs")
+    if dx is not None:
+        _bf16_cuda(dx, "dx", shape=(M, H), device=dev)
+    with_dp = dprobs is not None or want_dprobs
+    if workspace is not None:
+        _workspace(workspace, dgrad_glu_workspace_bytes(M, F, with_dp), dev)
     if dprobs is None and want_dprobs:
-        dprobs = torch.empty(M, dtype=torch.float32, device=dy.device)
-    dprobs = _probs_cuda(dprobs, M, "dprobs")
-    if workspace is None:
-        workspace = torch.empty(dgrad_glu_workspace_bytes(M, F, dprobs is not None), dtype=torch.uint8,
-                                device=dy.device)
-    if dx is None:
-        dx = torch.empty(M, H, dtype=torch.bfloat16, device=dy.device)
-    _check(lib.gg_dgrad_glu(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+        dprobs = torch.empty(M, dtype=torch.float32, device=dev)
+    workspace = _workspace(workspace, dgrad_glu_workspace_bytes(M, F, with_dp), dev)
+    dx = _out(dx, (M, H), "dx", dev)
+    _check(lib.gg_dgrad_glu(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr), E, H, F,
                             _activation(activation), _ptr(pr), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
                             _stream_ptr(stream)), "gg_dgrad_glu")
@@ -315,29 +423,31 @@ def gg_dgrad_recompute(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor,
                        E: int, H: int, F: int, activation="swiglu", probs: Optional[torch.Tensor] = None,
                        want_dprobs: bool = False, workspace: Optional[torch.Tensor] = None,
                        dx: Optional[torch.Tensor] = None, dprobs: Optional[torch.Tensor] = None,
-                       stream: Optional[torch.cuda.Stream] = None
+                       frag: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Input gradient without a saved H1: FC1 is recomputed from the forward
     input x [M, H] inside the call -> (dx, dprobs or None).  The workspace
     ends up holding dH1 [M, 2F] bf16 at its start."""
     _bf16_cuda(dy, "dy")
-    _bf16_cuda(x, "x")
-    _bf16_cuda(packed, "packed")
-    M = dy.shape[0]
-    if dy.shape != (M, H) or x.shape != (M, H):
-        raise ValueError("dy and x must be [M, H]")
-    off = _offsets(offsets, E)
-    pr = _probs_cuda(probs, M)
+    M, dev = dy.shape[0], dy.device
+    _bf16_cuda(dy, "dy", shape=(M, H))
+    _bf16_cuda(x, "x", shape=(M, H), device=dev)
+    _packed(packed, E, H, F, dev)
+    fr = _frag(frag, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    pr = _probs_cuda(probs, M, dev)
+    dprobs = _probs_cuda(dprobs, M, dev, "dprobs")
+    if dx is not None:
+        _bf16_cuda(dx, "dx", shape=(M, H), device=dev)
+    with_dp = dprobs is not None or want_dprobs
+    if workspace is not None:
+        _workspace(workspace, dgrad_glu_workspace_bytes(M, F, with_dp), dev)
     if dprobs is None and want_dprobs:
-        dprobs = torch.empty(M, dtype=torch.float32, device=dy.device)
-    dprobs = _probs_cuda(dprobs, M, "dprobs")
-    if workspace is None:
-        workspace = torch.empty(dgrad_glu_workspace_bytes(M, F, dprobs is not None), dtype=torch.uint8,
-                                device=dy.device)
-    if dx is None:
-        dx = torch.empty(M, H, dtype=torch.bfloat16, device=dy.device)
-    _check(lib.gg_dgrad_recompute(dy.data_ptr(), x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
-                                  _activation(activation), _ptr(pr), workspace.data_ptr(),
+        dprobs = torch.empty(M, dtype=torch.float32, device=dev)
+    workspace = _workspace(workspace, dgrad_glu_workspace_bytes(M, F, with_dp), dev)
+    dx = _out(dx, (M, H), "dx", dev)
+    _check(lib.gg_dgrad_recompute(dy.data_ptr(), x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr),
+                                  E, H, F, _activation(activation), _ptr(pr), workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
                                   _stream_ptr(stream)), "gg_dgrad_recompute")
     return dx, dprobs

@@ -23,6 +23,7 @@ namespace {
 struct DeviceInfo {
     int checked = 0;      // 0 unknown, 1 gfx950, -1 other
     int num_cu = 0;
+    int device = 0;       // device index
 };
 
 constexpr int kMaxDevices = 64;
@@ -48,6 +49,7 @@ int device_info(hipStream_t stream, DeviceInfo* out) {
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GG_ERR_HIP;
         const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         d.num_cu = prop.multiProcessorCount;
+        d.device = dev;
         d.checked = ok ? 1 : -1;
     }
     if (d.checked != 1) return GG_ERR_UNSUPPORTED_DEVICE;
@@ -93,13 +95,11 @@ int check_aliasing(const std::vector<Range>& ins, const std::vector<Range>& outs
     return GG_OK;
 }
 
-// Optional synchronous check of the device offsets (GG_DEBUG_VALIDATE=1).
+// Optional synchronous check of the device offsets (GG_DEBUG_VALIDATE=1, read
+// at every call so that a process can switch it on and off).
 int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStream_t stream) {
-    static const bool on = [] {
-        const char* v = std::getenv("GG_DEBUG_VALIDATE");
-        return v && v[0] == '1';
-    }();
-    if (!on) return GG_OK;
+    const char* v = std::getenv("GG_DEBUG_VALIDATE");
+    if (!(v && v[0] == '1')) return GG_OK;
     std::vector<int64_t> h(static_cast<size_t>(E + 1));
     if (hipMemcpyAsync(h.data(), offsets, sizeof(int64_t) * (E + 1), hipMemcpyDeviceToHost, stream) !=
             hipSuccess ||
@@ -111,11 +111,26 @@ int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStre
     return GG_OK;
 }
 
-// Shapes whose packed buffer also holds the fragment-ordered copies (W1, W2,
-// W1^T) read by the four-wave tiles of FC1, FC2 and dX.
+// Shapes that have fragment-ordered copies (W1, W2, W1^T, read by the
+// four-wave tiles of FC1, FC2 and dX).
 bool has_frag(int64_t H, int64_t F) { return H % 256 == 0 && F % 128 == 0; }
-// Elements of one expert block of the packed buffer.
-int64_t expert_block(int64_t H, int64_t F) { return (has_frag(H, F) ? 8 : 3) * F * H; }
+// Elements of one expert block of the packed buffer, and of the fragment buffer.
+int64_t expert_block(int64_t H, int64_t F) { return 3 * F * H; }
+int64_t frag_block(int64_t H, int64_t F) { return gg::FRAG_BLOCK_FH * F * H; }
+
+// Checks of an optional fragment buffer: null (no copies), or a 16-byte
+// aligned buffer for a shape that has them.
+int check_frag(const void* frag, int64_t H, int64_t F) {
+    if (!frag) return GG_OK;
+    if (!has_frag(H, F)) return GG_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(frag) & 15u) != 0) return GG_ERR_MISALIGNED;
+    return GG_OK;
+}
+
+// This GEMM's matrix in the fragment buffer (offset in units of F * H), or null.
+const uint16_t* frag_matrix(const void* frag, int which, int64_t H, int64_t F) {
+    return frag ? static_cast<const uint16_t*>(frag) + static_cast<int64_t>(which) * F * H : nullptr;
+}
 
 gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed, int64_t E,
                            int64_t H, int64_t F) {
@@ -125,6 +140,7 @@ gg::GemmParams base_params(const int64_t* offsets, int64_t M, const void* packed
     p.E = static_cast<int>(E);
     p.w_expert_stride = expert_block(H, F);
     p.w = static_cast<const uint16_t*>(packed);
+    p.wfrag_stride = frag_block(H, F);
     p.up_off = static_cast<int>(F);
     p.slope = 1.0f;
     return p;
@@ -177,6 +193,11 @@ size_t gg_dgrad_glu_workspace_bytes(int64_t M, int64_t F, int with_dprobs) {
     return n;
 }
 
+size_t gg_frag_bytes(int64_t E, int64_t H, int64_t F) {
+    if (E <= 0 || H <= 0 || F <= 0 || !has_frag(H, F)) return 0;
+    return static_cast<size_t>(2) * static_cast<size_t>(E) * static_cast<size_t>(frag_block(H, F));
+}
+
 int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, const void* const* w2,
                     void* packed, size_t packed_bytes, hipStream_t stream) {
     if (E < 1 || E > GG_MAX_EXPERTS || H <= 0 || F <= 0 || (H % 8) || (F % 8))
@@ -212,26 +233,43 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F, const void* const* w1, cons
             hipMemcpyAsync(d2, w2[e], w2_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return GG_ERR_HIP;
     }
-    if (has_frag(H, F) &&
-        gg::launch_pack_frag(static_cast<uint16_t*>(packed), static_cast<int>(E), static_cast<int>(H),
-                             static_cast<int>(F), stream) != hipSuccess)
-        return GG_ERR_HIP;
     return GG_OK;
+}
+
+int gg_pack_frag(int64_t E, int64_t H, int64_t F, const void* packed, size_t packed_bytes, void* frag,
+                 size_t frag_bytes, hipStream_t stream) {
+    if (E < 1 || E > GG_MAX_EXPERTS || H <= 0 || F <= 0 || (H % 8) || (F % 8) || !has_frag(H, F))
+        return GG_ERR_INVALID_ARGUMENT;
+    if (!packed || !frag) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(packed) || !aligned16(frag)) return GG_ERR_MISALIGNED;
+    if (packed_bytes < gg_packed_bytes(E, H, F) || frag_bytes < gg_frag_bytes(E, H, F))
+        return GG_ERR_WORKSPACE_TOO_SMALL;
+    if (overlap(range_of(packed, gg_packed_bytes(E, H, F)), range_of(frag, gg_frag_bytes(E, H, F))))
+        return GG_ERR_ALIASING;
+    DeviceInfo info;
+    const int st = device_info(stream, &info);
+    if (st != GG_OK) return st;
+    return gg::launch_pack_frag(static_cast<const uint16_t*>(packed), static_cast<uint16_t*>(frag),
+                                static_cast<int>(E), static_cast<int>(H), static_cast<int>(F), stream) == hipSuccess
+               ? GG_OK
+               : GG_ERR_HIP;
 }
 
 int gg_forward_fc1_swiglu(const void* x, const int64_t* offsets, int64_t M, const void* packed,
                           int64_t E, int64_t H, int64_t F, void* h1_out, void* a_out,
                           hipStream_t stream) {
-    return gg_forward_fc1_glu(x, offsets, M, packed, E, H, F, GG_ACT_SWIGLU, nullptr, h1_out, a_out, stream);
+    return gg_forward_fc1_glu(x, offsets, M, packed, nullptr, E, H, F, GG_ACT_SWIGLU, nullptr, h1_out, a_out,
+                              stream);
 }
 
-int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const void* packed, int64_t E,
-                       int64_t H, int64_t F, int activation, const float* probs, void* h1_out, void* a_out,
-                       hipStream_t stream) {
+int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const void* packed, const void* frag,
+                       int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* h1_out,
+                       void* a_out, hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
     const float slope = act_slope(activation);
     if (slope == 0.0f) return GG_ERR_INVALID_ARGUMENT;
+    if ((st = check_frag(frag, H, F)) != GG_OK) return st;
     if (M == 0) return GG_OK;
     if (!x || !offsets || !packed || !a_out) return GG_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(packed) || !aligned16(a_out) || (h1_out && !aligned16(h1_out)) ||
@@ -240,6 +278,7 @@ int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const v
     std::vector<Range> ins = {range_of(x, M * H * 2), range_of(packed, gg_packed_bytes(E, H, F)),
                               range_of(offsets, (E + 1) * 8)};
     if (probs) ins.push_back(range_of(probs, M * 4));
+    if (frag) ins.push_back(range_of(frag, gg_frag_bytes(E, H, F)));
     std::vector<Range> outs = {range_of(a_out, M * F * 2)};
     if (h1_out) outs.push_back(range_of(h1_out, M * 2 * F * 2));
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
@@ -255,20 +294,27 @@ int gg_forward_fc1_glu(const void* x, const int64_t* offsets, int64_t M, const v
     p.out1 = static_cast<uint16_t*>(h1_out);
     p.slope = slope;
     p.probs = probs;
-    if (has_frag(H, F)) p.wfrag = static_cast<const uint16_t*>(packed) + 3 * F * H;
+    p.wfrag = frag_matrix(frag, gg::FRAG_W1, H, F);
     return gg::launch_fc1_swiglu(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
 int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void* packed, int64_t E,
                    int64_t H, int64_t F, void* y, hipStream_t stream) {
+    return gg_forward_fc2_frag(a, offsets, M, packed, nullptr, E, H, F, y, stream);
+}
+
+int gg_forward_fc2_frag(const void* a, const int64_t* offsets, int64_t M, const void* packed, const void* frag,
+                        int64_t E, int64_t H, int64_t F, void* y, hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
+    if ((st = check_frag(frag, H, F)) != GG_OK) return st;
     if (M == 0) return GG_OK;
     if (!a || !offsets || !packed || !y) return GG_ERR_INVALID_ARGUMENT;
     if (!aligned16(a) || !aligned16(packed) || !aligned16(y) || (reinterpret_cast<uintptr_t>(offsets) & 7u))
         return GG_ERR_MISALIGNED;
     std::vector<Range> ins = {range_of(a, M * F * 2), range_of(packed, gg_packed_bytes(E, H, F)),
                               range_of(offsets, (E + 1) * 8)};
+    if (frag) ins.push_back(range_of(frag, gg_frag_bytes(E, H, F)));
     std::vector<Range> outs = {range_of(y, M * H * 2)};
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
     DeviceInfo info;
@@ -281,15 +327,15 @@ int gg_forward_fc2(const void* a, const int64_t* offsets, int64_t M, const void*
     p.N = static_cast<int>(H);
     p.ldw = static_cast<int>(F);
     p.out0 = static_cast<uint16_t*>(y);
-    if (has_frag(H, F)) p.wfrag = static_cast<const uint16_t*>(packed) + 5 * F * H;
+    p.wfrag = frag_matrix(frag, gg::FRAG_W2, H, F);
     return gg::launch_fc2(p, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
 int gg_dgrad(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
              int64_t E, int64_t H, int64_t F, void* workspace, size_t workspace_bytes, void* dx,
              hipStream_t stream) {
-    return gg_dgrad_glu(dy, h1, offsets, M, packed, E, H, F, GG_ACT_SWIGLU, nullptr, workspace, workspace_bytes,
-                        dx, nullptr, stream);
+    return gg_dgrad_glu(dy, h1, offsets, M, packed, nullptr, E, H, F, GG_ACT_SWIGLU, nullptr, workspace,
+                        workspace_bytes, dx, nullptr, stream);
 }
 
 }  // extern "C"
@@ -299,12 +345,14 @@ namespace {
 // Input gradient from the saved H1 (h1 != null) or from X, recomputing H1 into
 // the workspace first (x != null; exactly one of the two is given).
 int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* offsets, int64_t M,
-               const void* packed, int64_t E, int64_t H, int64_t F, int activation, const float* probs,
-               void* workspace, size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+               const void* packed, const void* frag, int64_t E, int64_t H, int64_t F, int activation,
+               const float* probs, void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
+               hipStream_t stream) {
     int st = check_shape(M, E, H, F);
     if (st != GG_OK) return st;
     const float slope = act_slope(activation);
     if (slope == 0.0f) return GG_ERR_INVALID_ARGUMENT;
+    if ((st = check_frag(frag, H, F)) != GG_OK) return st;
     if (M == 0) return GG_OK;
     const void* src = h1 ? h1 : x;   // the saved H1 [M][2F], or X [M][H]
     if (!dy || !src || !offsets || !packed || !workspace || !dx) return GG_ERR_INVALID_ARGUMENT;
@@ -317,6 +365,7 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
     std::vector<Range> ins = {range_of(dy, M * H * 2), range_of(src, h1 ? M * 2 * F * 2 : M * H * 2),
                               range_of(packed, gg_packed_bytes(E, H, F)), range_of(offsets, (E + 1) * 8)};
     if (probs) ins.push_back(range_of(probs, M * 4));
+    if (frag) ins.push_back(range_of(frag, gg_frag_bytes(E, H, F)));
     std::vector<Range> outs = {range_of(workspace, ws_need), range_of(dx, M * H * 2)};
     if (dprobs) outs.push_back(range_of(dprobs, M * 4));
     if ((st = check_aliasing(ins, outs)) != GG_OK) return st;
@@ -332,8 +381,8 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
         r.N = static_cast<int>(2 * F);
         r.ldw = static_cast<int>(H);
         r.out0 = static_cast<uint16_t*>(workspace);
-        if (has_frag(H, F)) {   // the four-wave kernel over W1's fragment copy, columns put back in H1 order
-            r.wfrag = static_cast<const uint16_t*>(packed) + 3 * F * H;
+        if (frag) {   // the four-wave kernel over W1's fragment copy, columns put back in H1 order
+            r.wfrag = frag_matrix(frag, gg::FRAG_W1, H, F);
             r.h1_order = 1;
         }
         if (gg::launch_fc2(r, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
@@ -368,7 +417,7 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
     q.N = static_cast<int>(H);
     q.ldw = static_cast<int>(H);
     q.out0 = static_cast<uint16_t*>(dx);
-    if (has_frag(H, F)) q.wfrag = static_cast<const uint16_t*>(packed) + 6 * F * H;   // W1^T fragments
+    q.wfrag = frag_matrix(frag, gg::FRAG_W1T, H, F);   // W1^T fragments: the same K-contiguous form
     return gg::launch_dgrad_fc1(q, info.num_cu, stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
@@ -377,18 +426,18 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
 extern "C" {
 
 int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
-                 int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
-                 size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+                 const void* frag, int64_t E, int64_t H, int64_t F, int activation, const float* probs,
+                 void* workspace, size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
     if (M > 0 && !h1) return GG_ERR_INVALID_ARGUMENT;
-    return dgrad_impl(dy, h1, nullptr, offsets, M, packed, E, H, F, activation, probs, workspace,
+    return dgrad_impl(dy, h1, nullptr, offsets, M, packed, frag, E, H, F, activation, probs, workspace,
                       workspace_bytes, dx, dprobs, stream);
 }
 
 int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, int64_t M, const void* packed,
-                       int64_t E, int64_t H, int64_t F, int activation, const float* probs, void* workspace,
-                       size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
+                       const void* frag, int64_t E, int64_t H, int64_t F, int activation, const float* probs,
+                       void* workspace, size_t workspace_bytes, void* dx, float* dprobs, hipStream_t stream) {
     if (M > 0 && !x) return GG_ERR_INVALID_ARGUMENT;
-    return dgrad_impl(dy, nullptr, x, offsets, M, packed, E, H, F, activation, probs, workspace,
+    return dgrad_impl(dy, nullptr, x, offsets, M, packed, frag, E, H, F, activation, probs, workspace,
                       workspace_bytes, dx, dprobs, stream);
 }
 

@@ -32,9 +32,10 @@ struct GemmParams {
     float* dp_part;            // derivative variant: partial sums of dp per row and
                                // 32-column group [M][dp_ld], or null
     int dp_ld;                 // ceil(N / 32)
-    // FC1, FC2 and dX: this GEMM's matrix in the fragment-ordered copy (same
-    // expert stride), or null.  With it, the GEMM runs in the four-wave kernel.
+    // FC1, FC2 and dX: this GEMM's matrix in the caller's fragment-ordered
+    // copy of the weights, or null.  With it, the GEMM runs in the four-wave kernel.
     const uint16_t* wfrag;
+    int64_t wfrag_stride;      // elements between consecutive experts in the fragment copy
     int h1_order;              // plain store over W1's fragment copy: write the columns in H1's gate | up order
 };
 
@@ -42,8 +43,12 @@ hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
-// Fragment-ordered copies of W1, W2 and W1^T inside every expert block (H % 256 == 0, F % 128 == 0).
-hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s);
+// Fragment-ordered copies of every expert's W1, W2 and W1^T (H % 256 == 0, F % 128 == 0),
+// written into `frag` (FRAG_BLOCK_FH * F * H elements per expert) from the row-major
+// packed buffer.
+constexpr int FRAG_BLOCK_FH = 5;
+constexpr int FRAG_W1 = 0, FRAG_W2 = 2, FRAG_W1T = 3;   // offsets within an expert block, in units of F*H
+hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 // dprobs[r] = sum over g of part[r][g] in increasing g, for the routed rows.
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,

@@ -8,9 +8,9 @@
 // with no rows own no tiles, so their weights are never read.
 //
 // Two kernels.  The eight-wave kernel (grouped_gemm_kernel) runs every GEMM
-// whose packed buffer has no fragment-ordered copies, and always the dgrad
-// FC2; the four-wave kernel (tile4_kernel, below) runs FC1, FC2 and dX over
-// those copies.  In the eight-wave kernel two flavors share one launch.  Rows
+// over the row-major packed weights, and always the dgrad FC2; the four-wave
+// kernel (tile4_kernel, below) runs FC1, FC2 and dX when the caller also
+// passes a fragment-ordered copy of the weights.  In the eight-wave kernel two flavors share one launch.  Rows
 // that fill 256-row tiles run as 256 x 256
 // output tiles; the at most 96 rows an expert leaves over (all rows of a
 // small expert) run as weight-streaming items, before the tiles.  An item is
@@ -1186,8 +1186,8 @@ void grouped_gemm_kernel(const GemmParams p) {
 
 // ---------------------------------------------------------------- four-wave kernel
 //
-// FC1, FC2 and dX over a fragment-ordered copy of the weights (present in the
-// packed buffer when H % 256 == 0 and F % 128 == 0), all in one launch: first
+// FC1, FC2 and dX over a fragment-ordered copy of the weights (an optional
+// buffer of the caller's, for H % 256 == 0 and F % 128 == 0), all in one launch: first
 // thin items (the at most 96 rows an expert leaves after its 256-row tiles,
 // or all rows of a small expert), then the tiles.  Four waves compute a
 // 256 x 256 tile: wave w owns token rows (w >> 1) * 128 .. +127 and weight rows
@@ -1297,7 +1297,7 @@ void tile4_kernel(const GemmParams p) {
         const int rows = re - row0;                          // 1 .. 96
         const int col0 = uni(local * TILE_COLS);
         const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
-        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.w_expert_stride;
+        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
         const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
         const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : tb0 + 1;
         auto wp = [&](int g, int j) -> const uint16_t* {
@@ -1450,7 +1450,7 @@ void tile4_kernel(const GemmParams p) {
         const int col0 = uni((local / tiles_m) * TILE_COLS);
         const int rows = min(TBM, row_end - row0);
         const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
-        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.w_expert_stride;
+        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
         // first 32-row block of this wave in fragment order
         const int rbw = (EPI == EPI_SWIGLU) ? (col0 / 64 + wn) * 4 : (col0 + wn * 128) / 32;
         auto wptr = [&](int g, int j) -> const uint16_t* {
@@ -1611,18 +1611,21 @@ void tile4_kernel(const GemmParams p) {
 }
 
 // Fragment-ordered copies (layout above) of every expert's W1 and W2 for the
-// forward tiles and of W1^T [H][2F] for dX = dH1 W1, written from the
-// row-major matrices of the same expert block (offsets 3FH, 5FH and 6FH).
-__global__ void pack_frag_kernel(uint16_t* __restrict__ packed, int E, int H, int F) {
-    const int64_t stride_e = 8LL * H * F;                       // elements per expert block
-    const int64_t c1 = 2LL * F * H / 8, c2 = 1LL * H * F / 8;   // 16-byte chunks per matrix
+// forward tiles and of W1^T [H][2F] for dX = dH1 W1, written into the
+// caller's fragment buffer (expert blocks of FRAG_BLOCK_FH * F * H elements:
+// W1 at FRAG_W1, W2 at FRAG_W2, W1^T at FRAG_W1T, in units of F * H) from the
+// row-major matrices of the packed buffer (expert blocks of 3 * F * H).
+__global__ void pack_frag_kernel(const uint16_t* __restrict__ packed, uint16_t* __restrict__ frag, int E, int H,
+                                 int F) {
+    const int64_t fh = static_cast<int64_t>(F) * H;
+    const int64_t c1 = 2 * fh / 8, c2 = fh / 8;                  // 16-byte chunks per matrix
     const int64_t per_e = 2 * c1 + c2;
     const int64_t total = static_cast<int64_t>(E) * per_e;
     const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
         const int e = static_cast<int>(i / per_e);
         int64_t ci = i - static_cast<int64_t>(e) * per_e;
-        uint16_t* blk = packed + e * stride_e;
+        const uint16_t* blk = packed + e * 3 * fh;                   // row-major W1_e, then W2_e
         const int which = ci < c1 ? 0 : (ci < c1 + c2 ? 1 : 2);   // W1, W2, W1^T
         ci -= which == 0 ? 0 : (which == 1 ? c1 : c1 + c2);
         const int K = which == 1 ? F : (which == 0 ? H : 2 * F);
@@ -1631,7 +1634,8 @@ __global__ void pack_frag_kernel(uint16_t* __restrict__ packed, int E, int H, in
         const int ks = static_cast<int>(rest % (K / 16));
         const int rbk = static_cast<int>(rest / (K / 16));
         const int k0 = ks * 16 + (l >> 5) * 8;
-        uint16_t* dst = blk + (which == 0 ? 3LL : (which == 1 ? 5LL : 6LL)) * F * H + ci * 8;
+        const int at = which == 0 ? FRAG_W1 : (which == 1 ? FRAG_W2 : FRAG_W1T);
+        uint16_t* dst = frag + e * FRAG_BLOCK_FH * fh + at * fh + ci * 8;
         if (which == 2) {   // row h of W1^T is column h of W1
             const int h = rbk * 32 + (l & 31);
             uint16_t v[8];
@@ -1648,7 +1652,7 @@ __global__ void pack_frag_kernel(uint16_t* __restrict__ packed, int E, int H, in
             const int q = rbk & 3, fb = rbk >> 2;
             row = (q < 2 ? 0 : F) + fb * 64 + (q & 1) * 32 + (l & 31);
         }
-        const uint16_t* src = blk + (which == 1 ? 2LL * F * H : 0) + static_cast<int64_t>(row) * K + k0;
+        const uint16_t* src = blk + (which == 1 ? 2 * fh : 0) + static_cast<int64_t>(row) * K + k0;
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
     }
 }
@@ -1723,12 +1727,13 @@ hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     if (!p.wfrag) return launch_cfg<false, EPI_STORE, false>(p, num_cu, s);
     return launch_tile4<EPI_STORE, false>(p, num_cu, s);
 }
-hipError_t launch_pack_frag(uint16_t* packed, int E, int H, int F, hipStream_t s) {
-    const int64_t chunks = static_cast<int64_t>(E) * 5 * H * F / 8;
+hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H, int F, hipStream_t s) {
+    const int64_t chunks = static_cast<int64_t>(E) * FRAG_BLOCK_FH * H * F / 8;
     int64_t blocks = (chunks + 255) / 256;
     if (blocks > 16384) blocks = 16384;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_frag_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, packed, E, H, F);
+    hipLaunchKernelGGL(pack_frag_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, packed, frag, E, H,
+                       F);
     return hipGetLastError();
 }
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {

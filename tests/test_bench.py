@@ -18,7 +18,8 @@ def test_cpu_baseline_on_the_tiny_workload():
     import bench
     import workload
     case = workload.draw_case(workload.by_name("tiny_e4_h64_f128"))
-    rec = bench.cpu_baseline(case, 0.2)
+    rec, sample = bench.cpu_baseline(case, 0.2)
+    assert sample["y"].shape == (sample["rows"].size, case.H)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1 and rec["seconds"] > 0
     assert "routed rows" in rec["sample"]

@@ -47,15 +47,108 @@ def test_header_compiles_as_c():
 
 
 def test_size_helpers():
+    """The packed buffer is exactly the weights, 6*E*H*F bytes, for every
+    shape; the fragment-ordered copies are a separate, opt-in buffer of
+    10*E*H*F bytes for shapes with H % 256 == 0 and F % 128 == 0 only."""
     gg = _gg()
+    import workload
     assert gg.packed_bytes(4, 64, 128) == 6 * 4 * 64 * 128
     assert gg.dgrad_workspace_bytes(512, 128) == 4 * 512 * 128
     assert gg.packed_bytes(0, 64, 128) == 0
-    # H % 256 == 0 and F % 128 == 0: each expert block also holds fragment-ordered copies
-    assert gg.packed_bytes(2, 256, 128) == 16 * 2 * 256 * 128
-    assert gg.packed_bytes(2, 256, 64) == 6 * 2 * 256 * 64
-    assert gg.packed_bytes(2, 384, 128) == 6 * 2 * 384 * 128
+    for E, H, F in ((2, 256, 128), (2, 256, 64), (2, 384, 128), (7, 512, 1024)):
+        assert gg.packed_bytes(E, H, F) == 6 * E * H * F
+    for w in workload.WORKLOADS:
+        assert gg.packed_bytes(w.E, w.H, w.F) == 6 * w.E * w.H * w.F
+    # the largest workload's weights take 6.4 GB by default
+    w = workload.by_name("padded_e128_h4096_f2048")
+    assert gg.packed_bytes(w.E, w.H, w.F) == 6442450944
+    assert gg.frag_bytes(2, 256, 128) == 10 * 2 * 256 * 128
+    assert gg.frag_bytes(2, 256, 64) == 0 and gg.frag_bytes(2, 384, 128) == 0
+    assert gg.frag_bytes(0, 256, 128) == 0
+    assert gg.has_frag(4096, 2048) and not gg.has_frag(2688, 1856)
     assert gg.lib.gg_status_string(5) == b"GG_ERR_ALIASING"
+
+
+def test_fragment_entry_points_validate_before_any_hip_call():
+    gg = _gg()
+    L = gg.lib
+    INV, MIS, WS, ALI = (gg.GG_ERR_INVALID_ARGUMENT, gg.GG_ERR_MISALIGNED,
+                         gg.GG_ERR_WORKSPACE_TOO_SMALL, gg.GG_ERR_ALIASING)
+    base = 1 << 40
+    E, H, F = 2, 256, 128
+    pk, fr = base, base + 2 ** 30
+    pb, fb = gg.packed_bytes(E, H, F), gg.frag_bytes(E, H, F)
+    # a shape without copies, null or misaligned buffers, sizes, overlap
+    assert L.gg_pack_frag(E, 264, F, pk, 1 << 30, fr, 1 << 30, None) == INV
+    assert L.gg_pack_frag(E, H, 136, pk, 1 << 30, fr, 1 << 30, None) == INV
+    assert L.gg_pack_frag(E, H, F, None, pb, fr, fb, None) == INV
+    assert L.gg_pack_frag(E, H, F, pk, pb, fr + 8, fb, None) == MIS
+    assert L.gg_pack_frag(E, H, F, pk, pb - 1, fr, fb, None) == WS
+    assert L.gg_pack_frag(E, H, F, pk, pb, fr, fb - 1, None) == WS
+    assert L.gg_pack_frag(E, H, F, pk, pb, pk + pb - 16, fb, None) == ALI
+    # the extended calls: a frag for a shape without copies, misaligned, or overlapping an output
+    M = 8
+    x, off, a, y = base + 2 ** 31, base + 2 ** 32, base + 2 ** 33, base + 2 ** 34
+    assert L.gg_forward_fc2_frag(a, off, M, pk, fr, E, 264, F, y, None) == INV
+    assert L.gg_forward_fc2_frag(a, off, M, pk, fr + 8, E, H, F, y, None) == MIS
+    assert L.gg_forward_fc2_frag(a, off, M, pk, fr, E, H, F, fr + 64, None) == ALI
+    assert L.gg_forward_fc1_glu(x, off, M, pk, fr, E, H, 136, 0, None, None, a, None) == INV
+    assert L.gg_forward_fc1_glu(x, off, M, pk, fr, E, H, F, 0, None, None, fr + fb - 16, None) == ALI
+    ws, dx = base + 2 ** 35, base + 2 ** 36
+    need = gg.dgrad_workspace_bytes(M, F)
+    assert L.gg_dgrad_glu(x, a, off, M, pk, fr + 4, E, H, F, 0, None, ws, need, dx, None, None) == MIS
+    assert L.gg_dgrad_glu(x, a, off, M, pk, fr, E, H, F, 0, None, ws, need, fr, None, None) == ALI
+    assert L.gg_dgrad_recompute(x, a, off, M, pk, fr, E, 264, F, 0, None, ws, need, dx, None, None) == INV
+    # empty batch: success without touching the pointers, a valid frag or not
+    assert L.gg_forward_fc2_frag(None, None, 0, None, None, E, H, F, None, None) == 0
+    assert L.gg_forward_fc2_frag(None, None, 0, None, fr, E, H, F, None, None) == 0
+
+
+def test_python_binding_checks_buffers_before_any_call():
+    """The binding refuses outputs, packed buffers, fragment buffers and
+    offsets of the wrong dtype, shape, contiguity or size with ValueError,
+    before any library call (the CPU tensors here would be refused for not
+    being device tensors, so the checks are reached through fakes that pass
+    the device test)."""
+    gg = _gg()
+    import torch
+
+    class FakeCuda(torch.Tensor):
+        """A CPU tensor that claims to be on the GPU (never reaches the library)."""
+        @property
+        def is_cuda(self):
+            return True
+
+        @property
+        def device(self):
+            return torch.device("cuda:0")
+
+    def fake(shape, dtype=torch.bfloat16):
+        return torch.zeros(*shape, dtype=dtype).as_subclass(FakeCuda)
+
+    E, H, F, M = 2, 64, 64, 16
+    x, off = fake((M, H)), fake((E + 1,), torch.int64)
+    packed = fake((gg.packed_bytes(E, H, F) // 2,))
+    with pytest.raises(ValueError, match="packed holds"):
+        gg.gg_forward_fc1_swiglu(x, off, fake((gg.packed_bytes(E, H, F) // 2 - 1,)), E, H, F)
+    with pytest.raises(ValueError, match="a_out must have shape"):
+        gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, a_out=fake((M, F + 8)))
+    with pytest.raises(ValueError, match="h1_out must be bfloat16"):
+        gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=fake((M, 2 * F), torch.float32))
+    with pytest.raises(ValueError, match="y must be contiguous"):
+        gg.gg_forward_fc2(fake((M, F)), off, packed, E, H, F, y=fake((H, M)).t())
+    with pytest.raises(ValueError, match="dx must have shape"):
+        gg.gg_dgrad(fake((M, H)), fake((M, 2 * F)), off, packed, E, H, F, dx=fake((M - 1, H)))
+    with pytest.raises(ValueError, match="workspace holds"):
+        gg.gg_dgrad(fake((M, H)), fake((M, 2 * F)), off, packed, E, H, F, workspace=fake((M, F)))
+    with pytest.raises(ValueError, match="offsets must be"):
+        gg.gg_forward_fc2(fake((M, F)), fake((E,), torch.int64), packed, E, H, F)
+    with pytest.raises(ValueError, match="no fragment-ordered copies"):
+        gg.gg_forward_fc2_frag(fake((M, F)), off, packed, fake((1024,)), E, H, F)
+    E2, H2, F2 = 2, 256, 128
+    with pytest.raises(ValueError, match="frag holds"):
+        gg.gg_forward_fc1_glu(fake((M, H2)), off, fake((gg.packed_bytes(E2, H2, F2) // 2,)), E2, H2, F2,
+                              frag=fake((gg.frag_bytes(E2, H2, F2) // 2 - 8,)))
 
 
 def test_validation_before_any_hip_call():
@@ -123,21 +216,21 @@ def test_glu_entry_points_validate_before_any_hip_call():
     assert gg.dgrad_glu_workspace_bytes(M, F, False) == 4 * M * F
     assert gg.dgrad_glu_workspace_bytes(M, F, True) == 4 * M * F + 4 * M * 5
     # empty batch and unknown activation (checked first)
-    assert L.gg_forward_fc1_glu(None, None, 0, None, 4, H, F, 0, None, None, None, None) == 0
-    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 2, None, h1, a, None) == INV
-    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, -1, None, h1, a, None) == INV
-    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 7, None, a, 1 << 20, base + 2 ** 35, None, None) == INV
+    assert L.gg_forward_fc1_glu(None, None, 0, None, None, 4, H, F, 0, None, None, None, None) == 0
+    assert L.gg_forward_fc1_glu(x, off, M, pk, None, 4, H, F, 2, None, h1, a, None) == INV
+    assert L.gg_forward_fc1_glu(x, off, M, pk, None, 4, H, F, -1, None, h1, a, None) == INV
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 7, None, a, 1 << 20, base + 2 ** 35, None, None) == INV
     # probs / dprobs must be 4-byte aligned
-    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 1, probs + 2, h1, a, None) == MIS
+    assert L.gg_forward_fc1_glu(x, off, M, pk, None, 4, H, F, 1, probs + 2, h1, a, None) == MIS
     ws, dx, dp = base + 2 ** 35, base + 2 ** 36, base + 2 ** 37
     need = gg.dgrad_glu_workspace_bytes(M, F, True)
-    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 1, probs, ws, need, dx, dp + 1, None) == MIS
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 1, probs, ws, need, dx, dp + 1, None) == MIS
     # the workspace must hold the partial sums when dprobs is given
-    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 1, probs, ws, need - 4, dx, dp, None) == WS
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 1, probs, ws, need - 4, dx, dp, None) == WS
     # aliasing: probs is an input, dprobs an output
-    assert L.gg_forward_fc1_glu(x, off, M, pk, 4, H, F, 0, a + 8, h1, a, None) == ALI
-    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 0, probs, ws, need, dx, ws + need - 4, None) == ALI
-    assert L.gg_dgrad_glu(x, h1, off, M, pk, 4, H, F, 0, probs, ws, need, dx, probs, None) == ALI
+    assert L.gg_forward_fc1_glu(x, off, M, pk, None, 4, H, F, 0, a + 8, h1, a, None) == ALI
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 0, probs, ws, need, dx, ws + need - 4, None) == ALI
+    assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 0, probs, ws, need, dx, probs, None) == ALI
 
 
 def test_python_binding_refuses_unsupported_weights():
@@ -154,16 +247,14 @@ def test_python_binding_refuses_unsupported_weights():
 
 
 def test_expert_views_slice_each_block():
-    """expert_views: W1_e at e*block, W2_e right after it, where one expert
-    block also holds the fragment-ordered copies when H % 256 == 0 and
-    F % 128 == 0 (host-side slicing only; a CPU tensor stands in for the
-    packed buffer)."""
+    """expert_views: W1_e at e*3FH, W2_e right after it (host-side slicing
+    only; a CPU tensor stands in for the packed buffer)."""
     import torch
     gg = _gg()
     for E, H, F in ((3, 64, 64), (3, 256, 128), (2, 512, 256)):
         n = gg.packed_bytes(E, H, F) // 2
         block = n // E
-        assert block == (8 if (H % 256 == 0 and F % 128 == 0) else 3) * F * H
+        assert block == 3 * F * H
         packed = torch.arange(n, dtype=torch.int64)
         w1, w2 = gg.expert_views(packed, E, H, F)
         for e in range(E):

@@ -40,7 +40,7 @@ def _layouts(R):
     }
 
 
-def _run(layout, R, base, weighted=False):
+def _run(layout, R, base, weighted=False, frag=False):
     xs, dys, counts, w1s, w2s, ps = [], [], [], [], [], []
     allp = torch.from_numpy(np.random.default_rng(77).uniform(0.05, 1.0, base.x.shape[0]).astype(np.float32))
     other = 0
@@ -66,7 +66,7 @@ def _run(layout, R, base, weighted=False):
     assert x.shape[0] == off[-1] and other <= base.x.shape[0] - R
     case = workload.Case("invariance", len(counts), base.H, base.F, int(counts.sum()), counts, off,
                          torch.stack(w1s), torch.stack(w2s), x, dy)
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, frag=frag)
     sl = slice(where, where + R)
     if not weighted:
         h1, a, y = dc.forward()
@@ -76,11 +76,11 @@ def _run(layout, R, base, weighted=False):
                 "dx": dx[sl].cpu()}
     gg = dc.gg
     probs = torch.cat(ps).to(dc.dev)
-    h1, a = gg.gg_forward_fc1_glu(dc.x, dc.offsets, dc.packed, dc.E, dc.H, dc.F, "qgeglu", probs)
-    y = gg.gg_forward_fc2(a, dc.offsets, dc.packed, dc.E, dc.H, dc.F)
+    h1, a = gg.gg_forward_fc1_glu(dc.x, dc.offsets, dc.packed, dc.E, dc.H, dc.F, "qgeglu", probs, frag=dc.frag)
+    y = gg.gg_forward_fc2_frag(a, dc.offsets, dc.packed, dc.frag, dc.E, dc.H, dc.F)
     ws = torch.empty(gg.dgrad_glu_workspace_bytes(dc.M, dc.F, True), dtype=torch.uint8, device=dc.dev)
     dx, dprobs = gg.gg_dgrad_glu(dc.dy, h1, dc.offsets, dc.packed, dc.E, dc.H, dc.F, "qgeglu", probs,
-                                 workspace=ws)
+                                 workspace=ws, frag=dc.frag)
     torch.cuda.synchronize()
     dh1 = ws[:4 * dc.M * dc.F].view(torch.bfloat16).view(dc.M, 2 * dc.F)
     return {"h1": h1[sl].cpu(), "a": a[sl].cpu(), "y": y[sl].cpu(), "dh1": dh1[sl].cpu(),
@@ -89,15 +89,19 @@ def _run(layout, R, base, weighted=False):
 
 @pytest.mark.parametrize("weighted", [False, True], ids=["swiglu", "weighted_qgeglu"])
 @pytest.mark.parametrize("H,F,R", [(256, 192, 40), (136, 200, 40), (256, 192, 64), (136, 200, 96),
-                                   (256, 128, 40), (256, 128, 96), (256, 256, 64)])   # the last three: four-wave tiles
+                                   (256, 128, 40), (256, 128, 96), (256, 256, 64)])   # the last three: also with fragment copies
 def test_rows_are_batch_invariant(H, F, R, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     base = workload.custom_case([R, 2400], H, F, seed=31)
     ref = None
-    for name, layout in _layouts(R).items():
-        log(f"[invariance] H={H} F={F} R={R} {name}")
-        got = _run(layout, R, base, weighted)
+    import moe_expert_grouped_ragged_amd as gg
+    for i, (name, layout) in enumerate(_layouts(R).items()):
+        # shapes with fragment-ordered copies alternate the weight layout, so
+        # the eight-wave and the four-wave kernels are compared as well
+        frag = gg.has_frag(H, F) and i % 2 == 1
+        log(f"[invariance] H={H} F={F} R={R} {name} frag={frag}")
+        got = _run(layout, R, base, weighted, frag)
         if ref is None:
             ref = got
             continue

@@ -21,7 +21,7 @@ CASES = [
     ([300, 0, 257, 40, 1], 128, 96),
     ([0, 520, 0], 72, 264),
     ([96, 95, 352, 0], 136, 200),   # three full 32-row blocks in streaming items
-    ([300, 0, 257, 40, 1, 97], 256, 128),   # four-wave forward tiles
+    ([300, 0, 257, 40, 1, 97], 256, 128),
 ]
 
 
@@ -29,32 +29,34 @@ def _probs(M, seed):
     return np.random.default_rng(seed).uniform(0.02, 1.0, M).astype(np.float32)
 
 
-def _run(c, act, probs_np, want_dprobs=True):
+def _run(c, act, probs_np, want_dprobs=True, frag=False):
     import moe_expert_grouped_ragged_amd as gg
     dev = torch.device("cuda:0")
     x, dy = c.x.to(dev), c.dy.to(dev)
     off = torch.from_numpy(np.ascontiguousarray(c.offsets)).to(dev)
     packed = gg.gg_pack_weights(c.w1.to(dev), c.w2.to(dev))
+    fr = gg.gg_pack_frag(packed, c.E, c.H, c.F) if frag else None
     probs = None if probs_np is None else torch.from_numpy(probs_np).to(dev)
-    h1, a = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs)
-    y = gg.gg_forward_fc2(a, off, packed, c.E, c.H, c.F)
+    h1, a = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs, frag=fr)
+    y = gg.gg_forward_fc2_frag(a, off, packed, fr, c.E, c.H, c.F)
     ws = torch.empty(gg.dgrad_glu_workspace_bytes(c.M, c.F, want_dprobs), dtype=torch.uint8, device=dev)
     dx, dprobs = gg.gg_dgrad_glu(dy, h1, off, packed, c.E, c.H, c.F, act, probs, want_dprobs=want_dprobs,
-                                 workspace=ws)
+                                 workspace=ws, frag=fr)
     torch.cuda.synchronize()
     dh1 = ws[:4 * c.M * c.F].view(torch.bfloat16).view(c.M, 2 * c.F)
     return h1, a, y, dh1, dx, dprobs
 
 
 @pytest.mark.parametrize("act", ["swiglu", "qgeglu"])
-@pytest.mark.parametrize("counts,H,F", CASES)
-def test_glu_stagewise_parity(act, counts, H, F):
+@pytest.mark.parametrize("counts,H,F,frag", [case + (False,) for case in CASES] +
+                         [([300, 0, 257, 40, 1, 97], 256, 128, True)])   # four-wave forward tiles and dX
+def test_glu_stagewise_parity(act, counts, H, F, frag):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     c = workload.custom_case(counts, H, F, seed=41)
     probs = _probs(c.M, 7)
-    log(f"[glu] act={act} counts={counts} H={H} F={F}")
-    h1, a, y, dh1, dx, dprobs = _run(c, act, probs)
+    log(f"[glu] act={act} counts={counts} H={H} F={F} frag={frag}")
+    h1, a, y, dh1, dx, dprobs = _run(c, act, probs, frag=frag)
     infos = stagewise_glu(c.x, c.dy, c.offsets, c.w1, c.w2, act, probs, h1, a, y, dh1, dx, dprobs)
     log("  " + " ".join(f"{i['name']}:{i.get('rel_l2', 0):.1e}" for i in infos))
 

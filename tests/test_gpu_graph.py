@@ -13,14 +13,15 @@ from gpu_harness import DeviceCase, log
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_follow_new_offsets():
+@pytest.mark.parametrize("H,F,frag", [(128, 96, False), (256, 128, True)])
+def test_graph_replays_follow_new_offsets(H, F, frag):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import moe_expert_grouped_ragged_amd as gg
     counts0 = [300, 0, 70, 20, 0, 513, 33, 1]
-    case = workload.custom_case(counts0, 128, 96, seed=21)
+    case = workload.custom_case(counts0, H, F, seed=21)
     E, H, F, M = case.E, case.H, case.F, case.M
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, frag=frag)
     dev = dc.dev
     off_dev = dc.offsets.clone()
     bufs = {"h1": torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev),
@@ -30,9 +31,10 @@ def test_graph_replays_follow_new_offsets():
             "dx": torch.empty(M, H, dtype=torch.bfloat16, device=dev)}
 
     def step(off, b):
-        gg.gg_forward_fc1_swiglu(dc.x, off, dc.packed, E, H, F, h1_out=b["h1"], a_out=b["a"])
-        gg.gg_forward_fc2(b["a"], off, dc.packed, E, H, F, y=b["y"])
-        gg.gg_dgrad(dc.dy, b["h1"], off, dc.packed, E, H, F, workspace=b["ws"], dx=b["dx"])
+        gg.gg_forward_fc1_glu(dc.x, off, dc.packed, E, H, F, h1_out=b["h1"], a_out=b["a"], frag=dc.frag)
+        gg.gg_forward_fc2_frag(b["a"], off, dc.packed, dc.frag, E, H, F, y=b["y"])
+        gg.gg_dgrad_glu(dc.dy, b["h1"], off, dc.packed, E, H, F, want_dprobs=False, workspace=b["ws"],
+                        dx=b["dx"], frag=dc.frag)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

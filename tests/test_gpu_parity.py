@@ -1,7 +1,9 @@
 """GPU parity of the HIP path against the CPU oracle (MI355X only).
 
 Same seeded inputs on both sides; forward (H1, A, Y) and input gradient
-(dH1, dX) compared element by element at the tolerance in parity.py.
+(dH1, dX) compared element by element at the tolerance in parity.py.  Shapes
+with fragment-ordered copies run both weight layouts (the packed buffer
+alone, and with the opt-in fragment buffer), which must agree bit for bit.
 """
 import numpy as np
 import pytest
@@ -9,8 +11,8 @@ import torch
 
 import oracle
 import workload
-from gpu_harness import DeviceCase, log
-from parity import DH1_ELEM_REL, check, check_chained, stagewise
+from gpu_harness import DeviceCase, bitwise_equal, layouts, log
+from parity import DH1_ELEM_REL, check, check_chained, stagewise, summary
 
 pytestmark = pytest.mark.gpu
 
@@ -20,14 +22,38 @@ def _gpu_ok():
         pytest.skip("no GPU")
 
 
+def run_layouts(case, canary: bool = True):
+    """Forward + dgrad in every layout the shape has; outputs pre-filled with
+    NaN canaries (an element a kernel never writes stays NaN and fails the
+    parity checks); the layouts must agree bit for bit.  Returns the first
+    layout's DeviceCase and outputs (h1, a, y, dH1, dx)."""
+    first = None
+    for frag in layouts(case.H, case.F):
+        log(f"[run] {case.name} E={case.E} H={case.H} F={case.F} M={case.M} frag={frag}")
+        dc = DeviceCase(case, frag=frag)
+        M, F, H = case.M, case.F, case.H
+        nan = float("nan")
+        fill = (lambda *shape: torch.full(shape, nan, dtype=torch.bfloat16, device=dc.dev)) if canary else \
+            (lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=dc.dev))
+        h1, a, y = dc.forward(h1_out=fill(M, 2 * F), a_out=fill(M, F), y=fill(M, H))
+        ws, dx = dc.dgrad(h1, workspace=fill(M, 2 * F), dx=fill(M, H))
+        torch.cuda.synchronize()
+        outs = (h1, a, y, ws, dx)
+        if first is None:
+            first = (dc, outs)
+        else:
+            for name, p, q in zip(("h1", "a", "y", "dh1", "dx"), first[1], outs):
+                assert bitwise_equal(p, q), f"{case.name}: {name} differs between the weight layouts"
+            log(f"[run] {case.name}: both weight layouts bitwise equal")
+            del dc
+    return first
+
+
 def run_full_parity(case):
-    """Whole-problem parity (every element), stage by stage."""
+    """Whole-problem parity (every element), stage by stage, in every layout."""
     _gpu_ok()
     log(f"[parity] {case.name} E={case.E} H={case.H} F={case.F} M={case.M} counts={list(case.counts)[:16]}")
-    dc = DeviceCase(case)
-    h1, a, y = dc.forward()
-    ws, dx = dc.dgrad(h1)
-    torch.cuda.synchronize()
+    dc, (h1, a, y, ws, dx) = run_layouts(case)
     rows = np.arange(int(case.offsets[0]), int(case.offsets[-1]))
     out = stagewise(case.x, case.dy, case.offsets, case.w1, case.w2, h1, a, y, ws, dx, rows)
     # dgrad from the oracle's H1 as well (same saved activation on both sides)
@@ -38,8 +64,7 @@ def run_full_parity(case):
     dref = oracle.dgrad(case.dy, ref["h1"], case.offsets, case.w1, case.w2)
     out += [check("dh1_from_oracle_h1", ws_o, dref["dh1"], rows, elem_rel=DH1_ELEM_REL),
             check_chained("dx_from_oracle_h1", dx_o, dref["dx"], rows)]
-    log(f"[parity] {case.name} ok: " + ", ".join(f"{o['name']} rl2={o.get('rel_l2', 0):.2e} "
-                                                  f"wr={o.get('worst_ratio', 0):.2f}" for o in out))
+    log(f"[parity] {case.name} ok: " + summary(out))
     return dc, (h1, a, y, dx)
 
 
@@ -182,13 +207,14 @@ def test_all_experts_empty_and_empty_batch():
     assert a0.shape == (0, F)
 
 
-def test_determinism_and_grouped_equals_per_expert():
+@pytest.mark.parametrize("H,F,frag", [(256, 192, False), (256, 128, False), (256, 128, True)])
+def test_determinism_and_grouped_equals_per_expert(H, F, frag):
     """Two runs are bitwise equal; a grouped call equals per-expert calls
-    (E = 1 views of the packed buffer) bitwise."""
+    (E = 1 views of the packed buffer, and of the fragment buffer) bitwise."""
     _gpu_ok()
     import moe_expert_grouped_ragged_amd as gg
-    case = workload.custom_case([70, 0, 300, 5], 256, 192, seed=13)
-    dc = DeviceCase(case)
+    case = workload.custom_case([70, 0, 300, 5], H, F, seed=13)
+    dc = DeviceCase(case, frag=frag)
     h1, a, y = dc.forward()
     ws, dx = dc.dgrad(h1)
     h1b, ab, yb = dc.forward()
@@ -197,28 +223,32 @@ def test_determinism_and_grouped_equals_per_expert():
     for p, q in ((h1, h1b), (a, ab), (y, yb), (ws, wsb), (dx, dxb)):
         assert torch.equal(p.view(torch.int16), q.view(torch.int16))
     per = gg.packed_bytes(1, case.H, case.F) // 2     # one expert block is an E = 1 packed buffer
+    fper = gg.frag_bytes(1, case.H, case.F) // 2      # and one fragment block an E = 1 fragment buffer
     for e in range(case.E):
         s, t = int(case.offsets[e]), int(case.offsets[e + 1])
         if s == t:
             continue
         pk = dc.packed[e * per:(e + 1) * per]
+        fr = dc.frag[e * fper:(e + 1) * fper] if frag else None
         off1 = torch.tensor([0, t - s], dtype=torch.int64, device="cuda")
-        h1e, ae = gg.gg_forward_fc1_swiglu(dc.x[s:t].contiguous(), off1, pk, 1, case.H, case.F)
-        ye = gg.gg_forward_fc2(ae, off1, pk, 1, case.H, case.F)
-        dxe = gg.gg_dgrad(dc.dy[s:t].contiguous(), h1e, off1, pk, 1, case.H, case.F)
+        h1e, ae = gg.gg_forward_fc1_glu(dc.x[s:t].contiguous(), off1, pk, 1, case.H, case.F, frag=fr)
+        ye = gg.gg_forward_fc2_frag(ae, off1, pk, fr, 1, case.H, case.F)
+        dxe, _ = gg.gg_dgrad_glu(dc.dy[s:t].contiguous(), h1e, off1, pk, 1, case.H, case.F, want_dprobs=False,
+                                 frag=fr)
         torch.cuda.synchronize()
         assert torch.equal(ye.view(torch.int16), y[s:t].view(torch.int16))
         assert torch.equal(dxe.view(torch.int16), dx[s:t].view(torch.int16))
 
 
-@pytest.mark.parametrize("H,F,counts", [(64, 64, [20, 30, 40]),
-                                         # fragment-ordered copies: re-packing rewrites them too
-                                         (256, 128, [120, 300, 40])])
-def test_repack_after_middle_expert_replaced(H, F, counts):
+@pytest.mark.parametrize("H,F,counts,frag", [(64, 64, [20, 30, 40], False),
+                                              (256, 128, [120, 300, 40], False),
+                                              # the fragment copies are re-derived after re-packing
+                                              (256, 128, [120, 300, 40], True)])
+def test_repack_after_middle_expert_replaced(H, F, counts, frag):
     _gpu_ok()
     import moe_expert_grouped_ragged_amd as gg
     case = workload.custom_case(counts, H, F, seed=17)
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, frag=frag)
     w1v, w2v = gg.expert_views(dc.packed, case.E, case.H, case.F)
     # views into the packed buffer re-pack as a no-op
     gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
@@ -227,6 +257,8 @@ def test_repack_after_middle_expert_replaced(H, F, counts):
     w1v = list(w1v)
     w1v[1] = new_w1                       # the middle expert is replaced by a new tensor
     gg.gg_pack_weights(w1v, w2v, packed=dc.packed)
+    if frag:
+        gg.gg_pack_frag(dc.packed, case.E, case.H, case.F, frag=dc.frag)
     y1 = dc.forward()[2]
     torch.cuda.synchronize()
     s1, t1 = int(case.offsets[1]), int(case.offsets[2])
@@ -237,75 +269,96 @@ def test_repack_after_middle_expert_replaced(H, F, counts):
     check("y_repacked", y1, ref["y"])
 
 
-def _sampled_rows(case, per_expert=3, max_experts=24, seed=0):
+def _tile_rows(case, n_random=512, seed=0):
+    """Rows that touch every 256-row tile of every expert: the first and the
+    last row of each tile, the first and last row of each expert and of its
+    real (unpadded) rows, one padding row, and random rows."""
     rng = np.random.default_rng(seed)
     off = case.offsets
-    live = [e for e in range(case.E) if off[e + 1] > off[e]]
-    sizes = np.array([off[e + 1] - off[e] for e in live])
-    pick = set(live[:2] + live[-2:] + [live[int(np.argmax(sizes))], live[int(np.argmin(sizes))]])
-    rest = [e for e in live if e not in pick]
-    rng.shuffle(rest)
-    pick = sorted(pick | set(rest[:max(0, max_experts - len(pick))]))
-    rows = []
-    for e in pick:
+    rows = set()
+    for e in range(case.E):
         s, t = int(off[e]), int(off[e + 1])
-        cand = {s, t - 1} | set(int(v) for v in rng.integers(s, t, per_expert))
-        rows += sorted(cand)
-    return np.array(sorted(set(rows)), dtype=np.int64)
+        if s == t:
+            continue
+        for r0 in range(s, t, 256):
+            rows |= {r0, min(r0 + 255, t - 1)}
+        real_end = s + int(case.counts[e])
+        rows |= {s, t - 1, max(s, real_end - 1)}
+        if real_end < t:
+            rows.add(real_end)
+    rows |= set(int(v) for v in rng.integers(int(off[0]), int(off[-1]), n_random))
+    return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["uniform_e32_h2048_f768", "zipf_e128_h2048_f768",
-                                  "smallbatch_e128_h2688_f1856", "padded_e128_h4096_f2048"])
-def test_workload_sampled_rows(name):
-    """Full-size workloads in the benchmark's launch configuration; the oracle
-    computes a sample of rows (first/last row of chosen experts plus random
-    rows), every row depending only on its own inputs and expert."""
+def _full_size_run(name, whole: bool):
     _gpu_ok()
     w = workload.by_name(name)
-    log(f"[sampled] drawing {name}")
+    log(f"[full] drawing {name}")
     case = workload.draw_case(w)
-    log(f"[sampled] {name} M={case.M}; running GPU")
-    dc = DeviceCase(case)
-    h1, a, y = dc.forward()
-    ws, dx = dc.dgrad(h1)
-    torch.cuda.synchronize()
-    rows = _sampled_rows(case)
-    log(f"[sampled] {name}: oracle on {rows.size} rows")
-    _, compact = oracle.sample_rows(case.offsets, rows)
-    rt = torch.from_numpy(rows)
-    rd = rt.to(dc.dev)
-    out = stagewise(case.x[rt], case.dy[rt], compact, case.w1, case.w2,
-                    h1[rd], a[rd], y[rd], ws[rd], dx[rd])
-    log(f"[sampled] {name} ok: " + ", ".join(f"{o['name']} rl2={o.get('rel_l2', 0):.2e} "
-                                             f"wr={o.get('worst_ratio', 0):.2f}" for o in out))
+    log(f"[full] {name} M={case.M}; running the GPU in every layout")
+    dc, (h1, a, y, ws, dx) = run_layouts(case, canary=True)
+    if whole:
+        rows = np.arange(int(case.offsets[0]), int(case.offsets[-1]))
+        log(f"[full] {name}: oracle on every one of the {rows.size} rows")
+        out = stagewise(case.x, case.dy, case.offsets, case.w1, case.w2, h1, a, y, ws, dx, rows)
+    else:
+        rows = _tile_rows(case)
+        log(f"[full] {name}: oracle on {rows.size} rows (both ends of every 256-row tile of every expert)")
+        _, compact = oracle.sample_rows(case.offsets, rows)
+        rt = torch.from_numpy(rows)
+        rd = rt.to(dc.dev)
+        out = stagewise(case.x[rt], case.dy[rt], compact, case.w1, case.w2,
+                        h1[rd], a[rd], y[rd], ws[rd], dx[rd])
+    log(f"[full] {name} ok: " + summary(out))
     # padding rows (if any) are exact zeros everywhere
     for e in range(case.E):
         pad = slice(int(case.offsets[e] + case.counts[e]), int(case.offsets[e + 1]))
         if pad.stop > pad.start:
-            assert int((y[pad].float() != 0).sum()) == 0 and int((dx[pad].float() != 0).sum()) == 0
-    log(f"[sampled] {name} ok")
+            for t in (h1, a, y, ws, dx):
+                assert int((t[pad].float() != 0).sum()) == 0
+    log(f"[full] {name} ok")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["uniform_e32_h2048_f768", "smallbatch_e128_h2688_f1856",
+                                  "zipf_e128_h2048_f768"])
+def test_workload_whole_output(name):
+    """Full-size workloads in the benchmark's launch configuration: every
+    element of H1, A, Y, dH1 and dX against the oracle, stage by stage and end
+    to end, in every weight layout."""
+    _full_size_run(name, whole=True)
+
+
+@pytest.mark.timeout(900)
+def test_padded_workload_every_tile():
+    """The largest workload (278,272 rows, H = 4096): the oracle computes both
+    ends of every 256-row tile of every expert, the padding boundaries and
+    random rows; the GPU runs the whole problem in every weight layout."""
+    _full_size_run("padded_e128_h4096_f2048", whole=False)
 
 
 def test_fragment_ordered_copies_layout():
-    """The packed buffer's fragment-ordered copies: block b of 32 weight rows
-    and k16 step s hold, for lane l, rows 32b + (l & 31) and k 16s + 8(l >> 5);
-    W1's blocks go gate, gate, up, up per 64 features; the third copy is W1^T."""
+    """The opt-in fragment buffer: per expert, W1 (rows in feature blocks of 64,
+    gate rows then up rows), W2 and W1^T, each in blocks of 32 rows x 16 k
+    where lane l holds rows 32b + (l & 31), k 16s + 8(l >> 5); the packed
+    buffer keeps exactly the row-major weights."""
     _gpu_ok()
     import moe_expert_grouped_ragged_amd as gg
     E, H, F = 3, 256, 128
     case = workload.custom_case([1, 2, 3], H, F, seed=5)
     w1, w2 = case.w1.cuda(), case.w2.cuda()
     packed = gg.gg_pack_weights(w1, w2)
+    frag = gg.gg_pack_frag(packed, E, H, F)
     torch.cuda.synchronize()
-    assert packed.numel() == 8 * E * H * F
-    blk = packed.view(E, 8 * H * F)
+    assert packed.numel() == 3 * E * H * F and frag.numel() == 5 * E * H * F
+    pblk = packed.view(E, 3 * H * F)
+    fblk = frag.view(E, 5 * H * F)
     for e in range(E):
-        assert torch.equal(blk[e, :2 * F * H].view(2 * F, H), w1[e])
-        assert torch.equal(blk[e, 2 * F * H:3 * F * H].view(H, F), w2[e])
-        # W1 rows in feature blocks of 64: gate rows then up rows
+        assert torch.equal(pblk[e, :2 * F * H].view(2 * F, H), w1[e])
+        assert torch.equal(pblk[e, 2 * F * H:].view(H, F), w2[e])
         w1i = torch.cat([w1[e][:F].view(F // 64, 64, H), w1[e][F:].view(F // 64, 64, H)], 1).reshape(2 * F, H)
-        for got, w, K in ((blk[e, 3 * F * H:5 * F * H], w1i, H), (blk[e, 5 * F * H:6 * F * H], w2[e], F),
-                          (blk[e, 6 * F * H:], w1[e].t().contiguous(), 2 * F)):
+        for got, w, K in ((fblk[e, :2 * F * H], w1i, H), (fblk[e, 2 * F * H:3 * F * H], w2[e], F),
+                          (fblk[e, 3 * F * H:], w1[e].t().contiguous(), 2 * F)):
             n = w.shape[0]
             want = w.reshape(n // 32, 32, K // 16, 2, 8).permute(0, 2, 3, 1, 4).reshape(-1)
             assert torch.equal(got, want)

@@ -19,32 +19,34 @@ pytestmark = pytest.mark.gpu
 
 CASES = [([5, 0, 7, 33], 64, 64), ([31, 32, 63, 64, 65, 0, 1], 136, 200), ([300, 0, 257, 40, 1], 128, 96),
          ([96, 95, 352, 0], 136, 200),
-         # four-wave forward tiles; the recompute's H1 comes from the eight-wave plain GEMM
+         # shapes with fragment copies (also run with them: four-wave forward tiles,
+         # the recompute's H1 over W1's fragment copy, four-wave dX)
          ([300, 0, 257, 40, 1, 97], 256, 128),
          ([300, 0, 257, 40, 1, 97], 256, 256)]
 MODES = [("swiglu", False), ("qgeglu", True)]
 
 
-def _both(c, act, weighted):
+def _both(c, act, weighted, frag=False):
     import moe_expert_grouped_ragged_amd as gg
     dev = torch.device("cuda:0")
     x, dy = c.x.to(dev), c.dy.to(dev)
     off = torch.from_numpy(np.ascontiguousarray(c.offsets)).to(dev)
     packed = gg.gg_pack_weights(c.w1.to(dev), c.w2.to(dev))
+    fr = gg.gg_pack_frag(packed, c.E, c.H, c.F) if frag else None
     probs = (torch.from_numpy(np.random.default_rng(3).uniform(0.05, 1, c.M).astype(np.float32)).to(dev)
              if weighted else None)
     nbytes = gg.dgrad_glu_workspace_bytes(c.M, c.F, weighted)
     # saved H1
-    h1, a = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs)
+    h1, a = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs, frag=fr)
     ws_s = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dx_s, dp_s = gg.gg_dgrad_glu(dy, h1, off, packed, c.E, c.H, c.F, act, probs, want_dprobs=weighted,
-                                 workspace=ws_s)
+                                 workspace=ws_s, frag=fr)
     # no saved H1
-    none, a_r = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs, save_h1=False)
+    none, a_r = gg.gg_forward_fc1_glu(x, off, packed, c.E, c.H, c.F, act, probs, save_h1=False, frag=fr)
     assert none is None
     ws_r = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=dev)
     dx_r, dp_r = gg.gg_dgrad_recompute(dy, x, off, packed, c.E, c.H, c.F, act, probs, want_dprobs=weighted,
-                                       workspace=ws_r)
+                                       workspace=ws_r, frag=fr)
     torch.cuda.synchronize()
     n = 4 * c.M * c.F
     return dict(h1=h1, a=a, a_r=a_r, dx_s=dx_s, dx_r=dx_r, dp_s=dp_s, dp_r=dp_r,
@@ -61,13 +63,14 @@ def _bitwise(out, weighted, rows=None):
 
 
 @pytest.mark.parametrize("act,weighted", MODES)
-@pytest.mark.parametrize("counts,H,F", CASES)
-def test_recompute_is_bitwise_the_saved_h1_path(counts, H, F, act, weighted):
+@pytest.mark.parametrize("counts,H,F,frag", [case + (False,) for case in CASES] +
+                         [case + (True,) for case in CASES if case[1] % 256 == 0 and case[2] % 128 == 0])
+def test_recompute_is_bitwise_the_saved_h1_path(counts, H, F, frag, act, weighted):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     c = workload.custom_case(counts, H, F, seed=51)
-    log(f"[recompute] {act} weighted={weighted} counts={counts} H={H} F={F}")
-    out = _both(c, act, weighted)
+    log(f"[recompute] {act} weighted={weighted} counts={counts} H={H} F={F} frag={frag}")
+    out = _both(c, act, weighted, frag)
     _bitwise(out, weighted)
     # end to end against the oracle (dX from dY and X through the recomputed H1)
     pr = None if not weighted else out_probs(c)
@@ -82,11 +85,12 @@ def out_probs(c):
     return np.random.default_rng(3).uniform(0.05, 1, c.M).astype(np.float32)
 
 
-@pytest.mark.parametrize("wl", ["uniform_e32_h2048_f768", "smallbatch_e128_h2688_f1856"])
-def test_recompute_full_size_bitwise(wl):
+@pytest.mark.parametrize("wl,frag", [("uniform_e32_h2048_f768", False), ("uniform_e32_h2048_f768", True),
+                                     ("smallbatch_e128_h2688_f1856", False)])
+def test_recompute_full_size_bitwise(wl, frag):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     c = workload.draw_case(workload.by_name(wl))
-    log(f"[recompute] full size {wl} M={c.M}")
-    out = _both(c, "swiglu", False)
+    log(f"[recompute] full size {wl} M={c.M} frag={frag}")
+    out = _both(c, "swiglu", False, frag)
     _bitwise(out, False)
