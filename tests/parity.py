@@ -100,10 +100,14 @@ def check_chained(name: str, got, ref, rows=None) -> dict:
 # different elements, so their counts and tails are samples of the same
 # rare-event process.  Asserted: the count over the bound, the relative L2 and
 # the 10th-largest ratio (a stable tail statistic) no worse than the oracle's
-# within sampling margins; the single worst element, a maximum over a few
-# dozen rare events, only within a looser factor.
+# within sampling margins (on small problems a single flip moves the relative
+# L2 by several percent, hence its absolute slack); the single worst element,
+# a maximum over a few dozen rare events, only within a looser factor.
 ACC_COUNT_FACTOR, ACC_COUNT_ABS = 1.5, 16
-ACC_REL_L2_FACTOR = 1.25
+# relative L2: one one-ulp flip of an element of typical size adds about
+# 2**-8 / sqrt(n) to it, so the slack is 1e-4 (5% of the 2e-3 bar) plus a few
+# such flips
+ACC_REL_L2_FACTOR, ACC_REL_L2_ABS, ACC_REL_L2_FLIPS = 1.25, 1e-4, 2.0 ** -6
 ACC_TAIL_K, ACC_TAIL_FACTOR = 10, 1.5
 ACC_WORST_FACTOR = 3.0
 
@@ -148,7 +152,8 @@ def check_not_less_accurate(name: str, gpu, orac, exact, rows=None) -> dict:
             "gpu_rel_l2": sg["rel_l2"], "oracle_rel_l2": so["rel_l2"]}
     assert sg["over_bound"] <= ACC_COUNT_FACTOR * so["over_bound"] + ACC_COUNT_ABS, \
         f"{name}: GPU has more elements over the bound than the oracle, against float64: {info}"
-    assert sg["rel_l2"] <= ACC_REL_L2_FACTOR * so["rel_l2"] + 1e-7, \
+    slack = ACC_REL_L2_ABS + ACC_REL_L2_FLIPS / np.sqrt(max(sg["n"], 1))
+    assert sg["rel_l2"] <= ACC_REL_L2_FACTOR * so["rel_l2"] + slack, \
         f"{name}: GPU relative L2 above the oracle's, against float64: {info}"
     assert tg <= ACC_TAIL_FACTOR * max(to, 1.0), \
         f"{name}: GPU tail (10th-largest ratio) above the oracle's, against float64: {info}"
