@@ -219,6 +219,22 @@ int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, in
                        void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
                        hipStream_t stream);
 
+/* ---- For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ * gg_dgrad without a workspace argument: dH1 goes to a static device array
+ * of the library, GG_NOALLOC_SCRATCH_BYTES bytes per GPU, allocated when the
+ * library's code is loaded on that GPU and held until the process ends.  The
+ * call allocates nothing and needs 4*M*F <= GG_NOALLOC_SCRATCH_BYTES
+ * (GG_ERR_WORKSPACE_TOO_SMALL otherwise; M*F <= 32 Mi elements).  Every call
+ * on one GPU uses that GPU's one array, so calls that overlap on one GPU
+ * (concurrent streams, or host threads) race and give undefined results:
+ * serialise them on one stream.  Nothing in the array needs clearing
+ * between calls.  Other arguments and results as gg_dgrad, bit for bit. */
+#define GG_NOALLOC_SCRATCH_BYTES (128u << 20)
+int gg_dgrad_noalloc(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
+                     const void* packed, int64_t E, int64_t H, int64_t F,
+                     void* dx, hipStream_t stream);
+
 /* Diagnostic: round n fp32 values to bf16 on the device with the same
  * conversion the epilogues use (lets a test check the device rounding
  * against round-to-nearest-even).  in: DEVICE float[n]; out: DEVICE

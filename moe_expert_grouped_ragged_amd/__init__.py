@@ -56,7 +56,7 @@ ACTIVATIONS = {"swiglu": GG_ACT_SWIGLU, "qgeglu": GG_ACT_QGEGLU}
 EXPORTED = ("gg_status_string", "gg_packed_bytes", "gg_dgrad_workspace_bytes", "gg_pack_weights",
             "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16",
             "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute",
-            "gg_frag_bytes", "gg_pack_frag", "gg_forward_fc2_frag")
+            "gg_frag_bytes", "gg_pack_frag", "gg_forward_fc2_frag", "gg_dgrad_noalloc")
 
 
 def _load() -> ctypes.CDLL:
@@ -80,6 +80,7 @@ def _load() -> ctypes.CDLL:
     lib.gg_forward_fc2_frag.argtypes = [p, p, i64, p, p, i64, i64, i64, p, p]
     lib.gg_dgrad.argtypes = [p, p, p, i64, p, i64, i64, i64, p, sz, p, p]
     lib.gg_round_bf16.argtypes = [p, p, i64, p]
+    lib.gg_dgrad_noalloc.argtypes = [p, p, p, i64, p, i64, i64, i64, p, p]
     lib.gg_dgrad_glu_workspace_bytes.argtypes = [i64, i64, i32]
     lib.gg_dgrad_glu_workspace_bytes.restype = sz
     lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, p, i64, i64, i64, i32, p, p, p, p]
@@ -87,7 +88,7 @@ def _load() -> ctypes.CDLL:
     lib.gg_dgrad_recompute.argtypes = [p, p, p, i64, p, p, i64, i64, i64, i32, p, p, sz, p, p, p]
     for name in ("gg_pack_weights", "gg_pack_frag", "gg_forward_fc1_swiglu", "gg_forward_fc2",
                  "gg_forward_fc2_frag", "gg_dgrad", "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu",
-                 "gg_dgrad_recompute"):
+                 "gg_dgrad_recompute", "gg_dgrad_noalloc"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -334,6 +335,27 @@ def gg_dgrad(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: 
     _check(lib.gg_dgrad(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                         dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad")
+    return dx
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20    # GG_NOALLOC_SCRATCH_BYTES of include/gg.h
+
+
+def gg_dgrad_noalloc(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor,
+                     E: int, H: int, F: int, dx: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """gg_dgrad with dH1 kept in the library's static per-GPU scratch (no
+    workspace; 4*M*F <= NOALLOC_SCRATCH_BYTES).  Calls that overlap on one GPU
+    race; with dx given, nothing is allocated."""
+    _bf16_cuda(dy, "dy")
+    M, dev = dy.shape[0], dy.device
+    _bf16_cuda(dy, "dy", shape=(M, H))
+    _bf16_cuda(h1, "h1", shape=(M, 2 * F), device=dev)
+    _packed(packed, E, H, F, dev)
+    off = _offsets(offsets, E, dev)
+    dx = _out(dx, (M, H), "dx", dev)
+    _check(lib.gg_dgrad_noalloc(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
+                                dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad_noalloc")
     return dx
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgg.so")
 
-SOURCES = ["gg_api.cpp", "gg_kernels.hip"]
+SOURCES = ["gg_api.cpp", "gg_kernels.hip", "gg_noalloc.hip"]
 HEADERS = ["gg_kernels.h"]
 
 # Packed-fp32 VALU ops are disabled for all device code.

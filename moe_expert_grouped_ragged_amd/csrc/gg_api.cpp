@@ -441,6 +441,23 @@ int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, in
                       workspace_bytes, dx, dprobs, stream);
 }
 
+int gg_dgrad_noalloc(const void* dy, const void* h1, const int64_t* offsets, int64_t M, const void* packed,
+                     int64_t E, int64_t H, int64_t F, void* dx, hipStream_t stream) {
+    int st = check_shape(M, E, H, F);
+    if (st != GG_OK) return st;
+    if (M == 0) return GG_OK;
+    if (gg_dgrad_workspace_bytes(M, F) > static_cast<size_t>(GG_NOALLOC_SCRATCH_BYTES))
+        return GG_ERR_WORKSPACE_TOO_SMALL;
+    if (!dy || !h1 || !offsets || !packed || !dx) return GG_ERR_INVALID_ARGUMENT;
+    DeviceInfo info;
+    if ((st = device_info(stream, &info)) != GG_OK) return st;
+    // dH1 goes to this device's copy of the static scratch array
+    void* scratch = nullptr;
+    if (gg::noalloc_scratch(info.device, &scratch) != hipSuccess) return GG_ERR_HIP;
+    return dgrad_impl(dy, h1, nullptr, offsets, M, packed, nullptr, E, H, F, GG_ACT_SWIGLU, nullptr, scratch,
+                      static_cast<size_t>(GG_NOALLOC_SCRATCH_BYTES), dx, nullptr, stream);
+}
+
 int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
     if (n < 0) return GG_ERR_INVALID_ARGUMENT;
     if (n == 0) return GG_OK;

@@ -50,6 +50,9 @@ constexpr int FRAG_BLOCK_FH = 5;
 constexpr int FRAG_W1 = 0, FRAG_W2 = 2, FRAG_W1T = 3;   // offsets within an expert block, in units of F*H
 hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+// Device address of the no-allocation scratch array (GG_NOALLOC_SCRATCH_BYTES)
+// on `device`, looked up once per device and cached (gg_noalloc.hip).
+hipError_t noalloc_scratch(int device, void** ptr);
 // dprobs[r] = sum over g of part[r][g] in increasing g, for the routed rows.
 hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* part, int ld, float* dprobs,
                             hipStream_t s);

@@ -257,6 +257,40 @@ static void test_pack() {
           GG_ERR_ALIASING);
 }
 
+static void test_noalloc() {
+    const int64_t E = 2, H = 256, F = 128, M = 33;
+    Buf dy(M * H * 2), h1(M * 2 * F * 2), off((E + 1) * 8), pk(gg_packed_bytes(E, H, F)), dx(M * H * 2);
+    g_launches.clear();
+    CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), M, pk.p, E, H, F, dx.p, fake_stream(1)) == GG_OK);
+    CHECK(g_launches.size() == 2);
+    if (g_launches.size() == 2) {
+        // dH1 in the device's scratch array, read back by the dX GEMM
+        uint16_t* scratch = g_launches[0].p.out0;
+        CHECK(scratch != nullptr && g_launches[1].p.act == scratch && g_launches[1].p.out0 == dx.as<uint16_t>());
+        CHECK((reinterpret_cast<uintptr_t>(scratch) & 15u) == 0);
+        // the same array on the next call on that device, another on another device
+        g_launches.clear();
+        CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), M - 5, pk.p, E, H, F, dx.p, fake_stream(1)) == GG_OK);
+        CHECK(g_launches.size() == 2 && g_launches[0].p.out0 == scratch);
+        g_launches.clear();
+        CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), M, pk.p, E, H, F, dx.p, fake_stream(2)) == GG_OK);
+        CHECK(g_launches.size() == 2 && g_launches[0].p.out0 != scratch);
+    }
+    // beyond the scratch size: refused before anything else; M == 0: nothing
+    g_launches.clear();
+    const int64_t big_m = (int64_t(GG_NOALLOC_SCRATCH_BYTES) / (4 * F)) + 1;
+    CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), big_m, pk.p, E, H, F, dx.p, fake_stream(1)) ==
+          GG_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), big_m - 1, pk.p, E, H, F, dx.p + 2, fake_stream(1)) ==
+          GG_ERR_MISALIGNED);
+    CHECK(gg_dgrad_noalloc(nullptr, nullptr, nullptr, 0, nullptr, E, H, F, nullptr, fake_stream(1)) == GG_OK);
+    CHECK(gg_dgrad_noalloc(dy.p, nullptr, off.as<int64_t>(), M, pk.p, E, H, F, dx.p, fake_stream(1)) ==
+          GG_ERR_INVALID_ARGUMENT);
+    CHECK(gg_dgrad_noalloc(dy.p, h1.p, off.as<int64_t>(), M, pk.p, E, H, F, dy.p + 64, fake_stream(1)) ==
+          GG_ERR_ALIASING);
+    CHECK(g_launches.empty());
+}
+
 int main() {
     test_sizes();
     test_argument_checks();
@@ -265,6 +299,7 @@ int main() {
     test_devices();
     test_debug_validate();
     test_pack();
+    test_noalloc();
     std::printf("api_driver: %d of %d checks failed\n", g_failed, g_checked);
     return g_failed == 0 ? 0 : 1;
 }

@@ -3,6 +3,8 @@
 // without a GPU.  Test infrastructure only.
 #include "launch_recorder.h"
 
+#include "gg.h"
+
 std::vector<Launch> g_launches;
 
 namespace gg {
@@ -27,6 +29,15 @@ hipError_t launch_round_bf16(const float*, uint16_t*, int64_t n, hipStream_t) {
 hipError_t launch_dp_reduce(const int64_t*, int E, int M, const float*, int ld, float*, hipStream_t) {
     Launch l{"dp_reduce", GemmParams{}, 0, nullptr, nullptr, E, M, ld};
     g_launches.push_back(l);
+    return hipSuccess;
+}
+// The static scratch array of the no-allocation entry point: one host buffer
+// per device here.
+hipError_t noalloc_scratch(int device, void** ptr) {
+    static std::vector<std::vector<uint8_t>> bufs(8);
+    if (device < 0 || device >= 8) return hipErrorInvalidDevice;
+    if (bufs[device].empty()) bufs[device].resize(GG_NOALLOC_SCRATCH_BYTES);
+    *ptr = bufs[device].data();
     return hipSuccess;
 }
 }  // namespace gg
