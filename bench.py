@@ -21,8 +21,8 @@ multiple of 256), hidden 4096, FFN 2048.
 
 Weights: the packed buffer alone (6*E*H*F bytes, the library's default) and,
 for shapes with H % 256 == 0 and F % 128 == 0, also with the opt-in
-fragment-ordered copies (gg_pack_frag, 10*E*H*F more bytes), which the
-extended calls take to run FC1, FC2 and dX in the four-wave kernel.  With
+fragment-ordered copies (gg_pack_frag, 12*E*H*F more bytes), which the
+extended calls take to run the GEMMs in the four-wave kernel.  With
 --layout auto both are timed, the same steps each; the line's headline is
 the copies' arm (the faster), and "layouts" gives both.
 
@@ -452,7 +452,7 @@ def main():
                    "routing": w.routing, "pad_to": w.pad_to,
                    "parallelism": "single-gpu", "activation": args.activation,
                    "weighted": bool(args.weighted), "recompute_fc1_in_dgrad": bool(args.recompute),
-                   "weights": ("packed buffer (6*E*H*F bytes) + opt-in fragment-ordered copies (10*E*H*F bytes)"
+                   "weights": ("packed buffer (6*E*H*F bytes) + opt-in fragment-ordered copies (12*E*H*F bytes)"
                                if arms[0] == "frag" else "packed buffer (6*E*H*F bytes)")},
         "timing": "median over the timed steps of HIP-event step times on the launch stream; a 1 GiB "
                   "scratch write before every step (outside the events) evicts the MALL and L2",

@@ -104,15 +104,15 @@ int gg_pack_weights(int64_t E, int64_t H, int64_t F,
 /* ---- Opt-in fragment-ordered weight copies (this library's own layout;
  * the pages pack only the original matrices).  For shapes with H % 256 == 0
  * and F % 128 == 0, a second, caller-owned buffer can hold copies of every
- * expert's W1, W2 and W1^T in the operand order of the CDNA4 bf16 matrix
- * instruction, which lets FC1, FC2 and the dX GEMM load their weight operands
+ * expert's W1, W2, W1^T and W2^T in the operand order of the CDNA4 bf16
+ * matrix instruction, which lets the four GEMMs load their weight operands
  * straight into registers.  The extended calls below take it as `frag`
- * (NULL: not used).  It costs 10*E*H*F more bytes (5/3 of the weights) and
- * buys about 8-12% on those GEMMs.  The copies are derived from the packed
+ * (NULL: not used).  It costs 12*E*H*F more bytes (twice the weights) and
+ * buys about 8-12% on FC1, FC2 and dX, more on dA.  The copies are derived from the packed
  * buffer by gg_pack_frag and do not follow later writes to it: call
  * gg_pack_frag again after re-packing. */
 
-/* Bytes of the fragment buffer: 10*E*H*F when H % 256 == 0 and F % 128 == 0,
+/* Bytes of the fragment buffer: 12*E*H*F when H % 256 == 0 and F % 128 == 0,
  * 0 for every other shape (no copies exist for it). */
 size_t gg_frag_bytes(int64_t E, int64_t H, int64_t F);
 
@@ -192,7 +192,8 @@ int gg_forward_fc2_frag(const void* a, const int64_t* offsets, int64_t M,
  * the partial sums).  Two launches on `stream`, three with dprobs.  With
  * GG_ACT_SWIGLU, probs == NULL and dprobs == NULL the results are those of
  * gg_dgrad, bit for bit.  `frag` as in gg_forward_fc1_glu (used by the dX
- * GEMM; the results do not depend on it). */
+ * GEMM, and by dA for plain SwiGLU with F % 256 == 0; the results do not
+ * depend on it). */
 int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
                  const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
                  int activation, const float* probs,

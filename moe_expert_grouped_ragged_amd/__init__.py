@@ -15,8 +15,8 @@ current stream.  The functions carry the C names:
   gg_pack_frag(packed, E, H, F)                  -> opt-in fragment buffer
   gg_forward_fc2_frag(a, offsets, packed, frag, ...) -> y
         (the *_glu, recompute and fc2_frag calls take `frag`: fragment-ordered
-        weight copies that speed up FC1, FC2 and dX for H % 256 == 0 and
-        F % 128 == 0, at 10*E*H*F more bytes)
+        weight copies that speed up the GEMMs for H % 256 == 0 and
+        F % 128 == 0, at 12*E*H*F more bytes)
 
 The *_glu calls add the QuickGeGLU activation and the weighting of the
 activation by each row's router probability (fp32 [M]), with dp of that

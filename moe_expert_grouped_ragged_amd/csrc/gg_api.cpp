@@ -111,8 +111,8 @@ int debug_validate_offsets(const int64_t* offsets, int64_t E, int64_t M, hipStre
     return GG_OK;
 }
 
-// Shapes that have fragment-ordered copies (W1, W2, W1^T, read by the
-// four-wave tiles of FC1, FC2 and dX).
+// Shapes that have fragment-ordered copies (W1, W2, W1^T, W2^T, read by the
+// four-wave tiles of FC1, FC2, dX and dA).
 bool has_frag(int64_t H, int64_t F) { return H % 256 == 0 && F % 128 == 0; }
 // Elements of one expert block of the packed buffer, and of the fragment buffer.
 int64_t expert_block(int64_t H, int64_t F) { return 3 * F * H; }
@@ -406,6 +406,7 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
                             : nullptr;
     p.dp_part = dp_part;
     p.dp_ld = static_cast<int>(dp_groups(F));
+    p.wfrag = frag_matrix(frag, gg::FRAG_W2T, H, F);   // W2^T fragments (four-wave tiles, plain SwiGLU)
     if (gg::launch_dgrad_fc2(p, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
     if (dprobs && gg::launch_dp_reduce(offsets, static_cast<int>(E), static_cast<int>(M), dp_part,
                                        static_cast<int>(dp_groups(F)), dprobs, stream) != hipSuccess)

@@ -32,8 +32,9 @@ struct GemmParams {
     float* dp_part;            // derivative variant: partial sums of dp per row and
                                // 32-column group [M][dp_ld], or null
     int dp_ld;                 // ceil(N / 32)
-    // FC1, FC2 and dX: this GEMM's matrix in the caller's fragment-ordered
-    // copy of the weights, or null.  With it, the GEMM runs in the four-wave kernel.
+    // This GEMM's matrix in the caller's fragment-ordered copy of the weights,
+    // or null.  With it, the GEMM runs in the four-wave kernel (dgrad FC2: the
+    // plain SwiGLU derivative with F a multiple of 256).
     const uint16_t* wfrag;
     int64_t wfrag_stride;      // elements between consecutive experts in the fragment copy
     int h1_order;              // plain store over W1's fragment copy: write the columns in H1's gate | up order
@@ -43,11 +44,14 @@ hipError_t launch_fc1_swiglu(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s);
 hipError_t launch_dgrad_fc1(const GemmParams& p, int num_cu, hipStream_t s);
-// Fragment-ordered copies of every expert's W1, W2 and W1^T (H % 256 == 0, F % 128 == 0),
-// written into `frag` (FRAG_BLOCK_FH * F * H elements per expert) from the row-major
-// packed buffer.
-constexpr int FRAG_BLOCK_FH = 5;
-constexpr int FRAG_W1 = 0, FRAG_W2 = 2, FRAG_W1T = 3;   // offsets within an expert block, in units of F*H
+// Fragment-ordered copies of every expert's W1, W2, W1^T and W2^T (H % 256 == 0,
+// F % 128 == 0), written into `frag` (FRAG_BLOCK_FH * F * H elements per expert)
+// from the row-major packed buffer.
+constexpr int FRAG_BLOCK_FH = 6;
+constexpr int FRAG_W1 = 0, FRAG_W2 = 2, FRAG_W1T = 3, FRAG_W2T = 5;   // offsets in an expert block, units of F*H
+// each matrix ends where the next begins (W1 2FH, W2 FH, W1^T 2FH, W2^T FH elements)
+static_assert(FRAG_W2 - FRAG_W1 == 2 && FRAG_W1T - FRAG_W2 == 1 && FRAG_W2T - FRAG_W1T == 2 &&
+                  FRAG_BLOCK_FH - FRAG_W2T == 1, "fragment block layout");
 hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 // Device address of the no-allocation scratch array (GG_NOALLOC_SCRATCH_BYTES)

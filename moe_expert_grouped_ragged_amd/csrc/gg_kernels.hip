@@ -1245,10 +1245,34 @@ __device__ __forceinline__ void wfrag_hold(bf16x8& a, bf16x8& b, bf16x8& c, bf16
     asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
 }
 
+// The plain SwiGLU derivative of four consecutive features of one token row,
+// in place: g, u are the saved bf16 gate and up values at pg and pu, the
+// results dG, dU overwrite them; dA = bf16(a[4q + x]).  The same arithmetic,
+// in the same order, as the eight-wave kernel's derivative epilogues.
+__device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, const f32x16& a, int q) {
+    const uint2 hg = *reinterpret_cast<const uint2*>(pg);
+    const uint2 hu = *reinterpret_cast<const uint2*>(pu);
+    const uint32_t gw[2] = {hg.x, hg.y};
+    const uint32_t uw[2] = {hu.x, hu.y};
+    float dg[4], du[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const float g = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
+        const float u = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
+        const float da = bf2f(f2bf(acc_rd(a[q * 4 + x])));
+        const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(1.0f * g)));
+        dg[x] = da * u * sgm * (1.0f + 1.0f * g * (1.0f - sgm));
+        du[x] = da * g * sgm;
+    }
+    *reinterpret_cast<uint2*>(pg) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+    *reinterpret_cast<uint2*>(pu) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+}
+
 template <int EPI, bool EXT>
 __global__ __launch_bounds__(T4_THREADS, 1)
 void tile4_kernel(const GemmParams p) {
-    static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues only");
+    static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU || (EPI == EPI_DSWIGLU && !EXT),
+                  "store, SwiGLU, and the plain SwiGLU derivative");
     const float slope = EXT ? p.slope : 1.0f;
     const float* const probs = EXT ? p.probs : nullptr;
     __shared__ __attribute__((aligned(1024))) uint16_t s_ring[T4_NSLOT * T4_SLOT];
@@ -1386,6 +1410,47 @@ void tile4_kernel(const GemmParams p) {
                 const int oc = p.h1_order ? h1_col(tb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
                 if (r < rows)
                     *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
+            }
+        } else if constexpr (EPI == EPI_DSWIGLU) {
+            // The saved gate and up values of the wave's 64 features for the
+            // item's rows, [96 rows][gate 64 | up 64] bf16 (256-byte rows,
+            // 24 KiB), are copied into the staging area with LDS-DMA (rows past
+            // the item repeat its last row); 16-byte chunk c (0..7 gate, 8..15
+            // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The results
+            // overwrite them in place and leave as whole row segments of dH1.
+            const int F = N;
+            const int f0 = col0 + 64 * wave + opaque;
+            const int ln = lane + opaque;     // per-lane values computed here, not above the K loop
+            const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
+            const uint32_t sl = lds_addr(stg);
+#pragma unroll
+            for (int d = 0; d < 24; ++d) {
+                const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                dma16(hb, static_cast<uint32_t>((min(r, rows - 1) * 2 * F + col) * 2), sl + d * 1024);
+            }
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int r = i * 32 + (ln & 31);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int pos = (4 * j + q) ^ (r & 7);
+                        uint16_t* pg = stg + r * 128 + pos * 8 + 4 * (ln >> 5);
+                        dswiglu_inplace(pg, pg + 64, acc[i][j], q);
+                    }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+            for (int d = 0; d < 24; ++d) {
+                const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 8);
+                const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * (2 * F) + col) = v;
             }
         } else {
             // [96 rows][32 features] bf16 arrays for A, gate and up; 16-byte
@@ -1547,6 +1612,76 @@ void tile4_kernel(const GemmParams p) {
                 if (wrow0 + r < row_end)
                     *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(wrow0 + r) * N + oc) = v;
             }
+        } else if constexpr (EPI == EPI_DSWIGLU) {
+            // SwiGLU derivative.  Per pass of 32 token rows (token block i) the
+            // saved gate and up values of the wave's 128 features,
+            // [32 rows][gate 128 | up 128] bf16 (512-byte rows, 16 KiB), are
+            // copied into one of two staging buffers with LDS-DMA (rows past
+            // the tile repeat its last row); 16-byte chunk c (0..15 gate, 16..31
+            // up) of row r sits at (c & 16) | ((c & 15) ^ (r & 15)).  The next
+            // pass's copy is in flight while a pass is computed in place and
+            // stored as whole row segments of dH1.  The waits count this wave's
+            // memory operations in issue order: 16 copies or 16 stores a pass.
+            const int F = N;
+            const int f0 = col0 + wn * 128 + opaque;
+            const int ln = lane + opaque;     // per-lane values computed here, not above the K loop
+            const int trows = rows + opaque;
+            const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
+            const uint32_t sl = lds_addr(stg);
+            auto h1_copy = [&](int pass, int buf) {
+#pragma unroll
+                for (int d = 0; d < 16; ++d) {
+                    const int r = 2 * d + (ln >> 5), pc = ln & 31;
+                    const int c = (pc & 16) | ((pc & 15) ^ (r & 15));
+                    const int trow = min(wg * 128 + pass * 32 + r, trows - 1);
+                    const int col = (c < 16 ? 0 : F) + f0 + 8 * (c & 15);
+                    dma16(hb, static_cast<uint32_t>((trow * 2 * F + col) * 2), sl + buf * 16384 + d * 1024);
+                }
+            };
+            auto h1_compute = [&](auto pass_tag, int buf) {
+                constexpr int i = decltype(pass_tag)::value;
+                const int r = ln & 31;
+                uint16_t* b = stg + buf * 8192;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int pos = (4 * j + q) ^ (r & 15);
+                        uint16_t* pg = b + r * 256 + pos * 8 + 4 * (ln >> 5);
+                        dswiglu_inplace(pg, pg + 128, acc[i][j], q);
+                    }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            };
+            auto h1_store = [&](int pass, int buf) {
+                const uint16_t* b = stg + buf * 8192;
+#pragma unroll
+                for (int d = 0; d < 16; ++d) {
+                    const int r = 2 * d + (ln >> 5), pc = ln & 31;
+                    const int c = (pc & 16) | ((pc & 15) ^ (r & 15));
+                    const uint4 v = *reinterpret_cast<const uint4*>(b + r * 256 + pc * 8);
+                    const int grow = wrow0 + pass * 32 + r;
+                    const int col = (c < 16 ? 0 : F) + f0 + 8 * (c & 15);
+                    if (grow < row_end) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * (2 * F) + col) = v;
+                }
+                // the buffer's reads are done before a copy refills it
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            };
+            h1_copy(0, 0);
+            h1_copy(1, 1);
+            wait_vmcnt<16>();                       // pass 0 has landed
+            h1_compute(GrpTag<0>{}, 0);
+            h1_store(0, 0);
+            h1_copy(2, 0);
+            wait_vmcnt<32>();                       // pass 1 (then the stores of pass 0, the copy of pass 2)
+            h1_compute(GrpTag<1>{}, 1);
+            h1_store(1, 1);
+            h1_copy(3, 1);
+            wait_vmcnt<32>();                       // pass 2
+            h1_compute(GrpTag<2>{}, 0);
+            h1_store(2, 0);
+            wait_vmcnt<16>();                       // pass 3
+            h1_compute(GrpTag<3>{}, 1);
+            h1_store(3, 1);
         } else {
             // per pass of 64 token rows, [64][64] bf16 arrays for A, gate and up;
             // 16-byte chunk c of row r at c ^ (r & 7)
@@ -1611,48 +1746,50 @@ void tile4_kernel(const GemmParams p) {
 }
 
 // Fragment-ordered copies (layout above) of every expert's W1 and W2 for the
-// forward tiles and of W1^T [H][2F] for dX = dH1 W1, written into the
-// caller's fragment buffer (expert blocks of FRAG_BLOCK_FH * F * H elements:
-// W1 at FRAG_W1, W2 at FRAG_W2, W1^T at FRAG_W1T, in units of F * H) from the
-// row-major matrices of the packed buffer (expert blocks of 3 * F * H).
+// forward tiles, of W1^T [H][2F] for dX = dH1 W1 and of W2^T [F][H] for
+// dA = dY W2, written into the caller's fragment buffer (expert blocks of
+// FRAG_BLOCK_FH * F * H elements: W1 at FRAG_W1, W2 at FRAG_W2, W1^T at
+// FRAG_W1T, W2^T at FRAG_W2T, in units of F * H) from the row-major matrices
+// of the packed buffer (expert blocks of 3 * F * H).
 __global__ void pack_frag_kernel(const uint16_t* __restrict__ packed, uint16_t* __restrict__ frag, int E, int H,
                                  int F) {
     const int64_t fh = static_cast<int64_t>(F) * H;
-    const int64_t c1 = 2 * fh / 8, c2 = fh / 8;                  // 16-byte chunks per matrix
-    const int64_t per_e = 2 * c1 + c2;
+    // One thread per 16-byte chunk of the fragment buffer.  A chunk's matrix
+    // follows from its element offset inside its expert block, so the writes
+    // cover exactly E * FRAG_BLOCK_FH * F * H elements.
+    const int64_t per_e = FRAG_BLOCK_FH * fh / 8;
     const int64_t total = static_cast<int64_t>(E) * per_e;
     const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
         const int e = static_cast<int>(i / per_e);
-        int64_t ci = i - static_cast<int64_t>(e) * per_e;
-        const uint16_t* blk = packed + e * 3 * fh;                   // row-major W1_e, then W2_e
-        const int which = ci < c1 ? 0 : (ci < c1 + c2 ? 1 : 2);   // W1, W2, W1^T
-        ci -= which == 0 ? 0 : (which == 1 ? c1 : c1 + c2);
-        const int K = which == 1 ? F : (which == 0 ? H : 2 * F);
+        const int64_t el = (i - static_cast<int64_t>(e) * per_e) * 8;    // element offset in the block
+        const int at = el < FRAG_W2 * fh ? FRAG_W1 : (el < FRAG_W1T * fh ? FRAG_W2 : (el < FRAG_W2T * fh ? FRAG_W1T : FRAG_W2T));
+        const int64_t ci = (el - at * fh) / 8;                           // chunk within its matrix
+        const uint16_t* blk = packed + e * 3 * fh;                       // row-major W1_e, then W2_e
+        const int K = at == FRAG_W1 ? H : (at == FRAG_W2 ? F : (at == FRAG_W1T ? 2 * F : H));
         const int l = static_cast<int>(ci & 63);
         const int64_t rest = ci >> 6;
         const int ks = static_cast<int>(rest % (K / 16));
         const int rbk = static_cast<int>(rest / (K / 16));
         const int k0 = ks * 16 + (l >> 5) * 8;
-        const int at = which == 0 ? FRAG_W1 : (which == 1 ? FRAG_W2 : FRAG_W1T);
-        uint16_t* dst = frag + e * FRAG_BLOCK_FH * fh + at * fh + ci * 8;
-        if (which == 2) {   // row h of W1^T is column h of W1
-            const int h = rbk * 32 + (l & 31);
+        uint16_t* dst = frag + e * FRAG_BLOCK_FH * fh + el;
+        const int row = rbk * 32 + (l & 31);
+        if (at == FRAG_W1T || at == FRAG_W2T) {   // row n of the transpose is column n of the matrix
+            const uint16_t* src = at == FRAG_W1T ? blk : blk + 2 * fh;   // W1 [2F][H] or W2 [H][F]
+            const int ld = at == FRAG_W1T ? H : F;
             uint16_t v[8];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) v[x] = blk[static_cast<int64_t>(k0 + x) * H + h];
+            for (int x = 0; x < 8; ++x) v[x] = src[static_cast<int64_t>(k0 + x) * ld + row];
             *reinterpret_cast<uint4*>(dst) = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16),
                                                         v[4] | (v[5] << 16), v[6] | (v[7] << 16));
             continue;
         }
-        int row;
-        if (which == 1) {
-            row = rbk * 32 + (l & 31);
-        } else {
+        int srow = row;
+        if (at == FRAG_W1) {
             const int q = rbk & 3, fb = rbk >> 2;
-            row = (q < 2 ? 0 : F) + fb * 64 + (q & 1) * 32 + (l & 31);
+            srow = (q < 2 ? 0 : F) + fb * 64 + (q & 1) * 32 + (l & 31);
         }
-        const uint16_t* src = blk + (which == 1 ? 2 * fh : 0) + static_cast<int64_t>(row) * K + k0;
+        const uint16_t* src = blk + (at == FRAG_W2 ? 2 * fh : 0) + static_cast<int64_t>(srow) * K + k0;
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
     }
 }
@@ -1736,7 +1873,12 @@ hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H
                        F);
     return hipGetLastError();
 }
+// The plain SwiGLU derivative runs on four-wave tiles over W2^T's fragment
+// copy when there is one and F is a multiple of the 256-column tile; the
+// weighted and QuickGeGLU variants, and every other shape, on the eight-wave
+// kernel (the same bits either way).
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
+    if (p.wfrag && plain_swiglu(p) && p.N % TBN == 0) return launch_tile4<EPI_DSWIGLU, false>(p, num_cu, s);
     return plain_swiglu(p) ? launch_cfg<true, EPI_DSWIGLU, false>(p, num_cu, s)
                            : launch_cfg<true, EPI_DSWIGLU, true>(p, num_cu, s);
 }

@@ -38,7 +38,7 @@ static void test_sizes() {
     CHECK(gg_packed_bytes(4, 64, 128) == size_t(6) * 4 * 64 * 128);
     CHECK(gg_packed_bytes(128, 4096, 2048) == size_t(6442450944ull));
     CHECK(gg_packed_bytes(0, 64, 128) == 0 && gg_packed_bytes(4, -8, 128) == 0);
-    CHECK(gg_frag_bytes(3, 256, 128) == size_t(10) * 3 * 256 * 128);
+    CHECK(gg_frag_bytes(3, 256, 128) == size_t(12) * 3 * 256 * 128);
     CHECK(gg_frag_bytes(3, 264, 128) == 0 && gg_frag_bytes(3, 256, 136) == 0);
     CHECK(gg_dgrad_workspace_bytes(10, 16) == 640 && gg_dgrad_workspace_bytes(0, 16) == 0);
     CHECK(gg_dgrad_glu_workspace_bytes(10, 40, 1) == 4 * 10 * 40 + 4 * 10 * 2);
@@ -59,12 +59,12 @@ static void test_forward_launches() {
     CHECK(p.w == pk.as<uint16_t>() && p.w_expert_stride == 3 * F * H && p.wfrag == nullptr);
     CHECK(p.out0 == a.as<uint16_t>() && p.out1 == h1.as<uint16_t>() && p.slope == 1.0f && !p.probs);
     CHECK(g_launches[0].num_cu == 256);
-    // with the fragment buffer: W1's copy at its start, expert stride 5FH
+    // with the fragment buffer: W1's copy at its start, expert stride 6FH
     g_launches.clear();
     CHECK(gg_forward_fc1_glu(x.p, off.as<int64_t>(), M, pk.p, fr.p, E, H, F, GG_ACT_QGEGLU, nullptr, nullptr,
                              a.p, s) == GG_OK);
     CHECK(g_launches.size() == 1 && g_launches[0].p.wfrag == fr.as<uint16_t>());
-    CHECK(g_launches[0].p.wfrag_stride == 5 * F * H && g_launches[0].p.slope == 1.702f);
+    CHECK(g_launches[0].p.wfrag_stride == 6 * F * H && g_launches[0].p.slope == 1.702f);
     CHECK(g_launches[0].p.out1 == nullptr);
     // FC2: W2 after W1 in both buffers
     g_launches.clear();
@@ -111,7 +111,8 @@ static void test_dgrad_launches() {
     if (g_launches.size() == 3) {
         CHECK(!std::strcmp(g_launches[1].kind, "dp_reduce") && g_launches[1].c == (F + 31) / 32);
         CHECK(g_launches[0].p.dp_part == reinterpret_cast<float*>(ws.p + gg_dgrad_workspace_bytes(M, F)));
-        CHECK(g_launches[2].p.wfrag == fr.as<uint16_t>() + 3 * F * H && g_launches[2].p.wfrag_stride == 5 * F * H);
+        CHECK(g_launches[2].p.wfrag == fr.as<uint16_t>() + 3 * F * H && g_launches[2].p.wfrag_stride == 6 * F * H);
+        CHECK(g_launches[0].p.wfrag == fr.as<uint16_t>() + 5 * F * H);   // W2^T for dA
     }
     // the workspace must hold the partial sums
     CHECK(gg_dgrad_glu(dy.p, h1.p, off.as<int64_t>(), M, pk.p, nullptr, E, H, F, 0, nullptr, ws.p,

@@ -49,7 +49,7 @@ def test_header_compiles_as_c():
 def test_size_helpers():
     """The packed buffer is exactly the weights, 6*E*H*F bytes, for every
     shape; the fragment-ordered copies are a separate, opt-in buffer of
-    10*E*H*F bytes for shapes with H % 256 == 0 and F % 128 == 0 only."""
+    12*E*H*F bytes for shapes with H % 256 == 0 and F % 128 == 0 only."""
     gg = _gg()
     import workload
     assert gg.packed_bytes(4, 64, 128) == 6 * 4 * 64 * 128
@@ -62,7 +62,7 @@ def test_size_helpers():
     # the largest workload's weights take 6.4 GB by default
     w = workload.by_name("padded_e128_h4096_f2048")
     assert gg.packed_bytes(w.E, w.H, w.F) == 6442450944
-    assert gg.frag_bytes(2, 256, 128) == 10 * 2 * 256 * 128
+    assert gg.frag_bytes(2, 256, 128) == 12 * 2 * 256 * 128
     assert gg.frag_bytes(2, 256, 64) == 0 and gg.frag_bytes(2, 384, 128) == 0
     assert gg.frag_bytes(0, 256, 128) == 0
     assert gg.has_frag(4096, 2048) and not gg.has_frag(2688, 1856)

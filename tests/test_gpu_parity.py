@@ -339,7 +339,7 @@ def test_padded_workload_every_tile():
 
 def test_fragment_ordered_copies_layout():
     """The opt-in fragment buffer: per expert, W1 (rows in feature blocks of 64,
-    gate rows then up rows), W2 and W1^T, each in blocks of 32 rows x 16 k
+    gate rows then up rows), W2, W1^T and W2^T, each in blocks of 32 rows x 16 k
     where lane l holds rows 32b + (l & 31), k 16s + 8(l >> 5); the packed
     buffer keeps exactly the row-major weights."""
     _gpu_ok()
@@ -350,15 +350,16 @@ def test_fragment_ordered_copies_layout():
     packed = gg.gg_pack_weights(w1, w2)
     frag = gg.gg_pack_frag(packed, E, H, F)
     torch.cuda.synchronize()
-    assert packed.numel() == 3 * E * H * F and frag.numel() == 5 * E * H * F
+    assert packed.numel() == 3 * E * H * F and frag.numel() == 6 * E * H * F
     pblk = packed.view(E, 3 * H * F)
-    fblk = frag.view(E, 5 * H * F)
+    fblk = frag.view(E, 6 * H * F)
     for e in range(E):
         assert torch.equal(pblk[e, :2 * F * H].view(2 * F, H), w1[e])
         assert torch.equal(pblk[e, 2 * F * H:].view(H, F), w2[e])
         w1i = torch.cat([w1[e][:F].view(F // 64, 64, H), w1[e][F:].view(F // 64, 64, H)], 1).reshape(2 * F, H)
         for got, w, K in ((fblk[e, :2 * F * H], w1i, H), (fblk[e, 2 * F * H:3 * F * H], w2[e], F),
-                          (fblk[e, 3 * F * H:], w1[e].t().contiguous(), 2 * F)):
+                          (fblk[e, 3 * F * H:5 * F * H], w1[e].t().contiguous(), 2 * F),
+                          (fblk[e, 5 * F * H:], w2[e].t().contiguous(), H)):
             n = w.shape[0]
             want = w.reshape(n // 32, 32, K // 16, 2, 8).permute(0, 2, 3, 1, 4).reshape(-1)
             assert torch.equal(got, want)
