@@ -3,9 +3,10 @@ plus the input gradient) on one MI355X.
 
 One step = gg_forward_fc1_swiglu (saving H1) + gg_forward_fc2 + gg_dgrad
 over one synthetic batch that is already resident in HBM.  Before every step
-(warm-up and timed) a 1 GiB scratch buffer is written, outside the timed
-events, so that no operand is left in the 256 MiB MALL or the L2 from the step
-before.  Each call is timed with HIP events on the launch stream; the step
+(warm-up and timed) a 1 GiB scratch buffer is written and another 1 GiB read,
+outside the timed events, so that no operand is left in the 256 MiB MALL or
+the L2 from the step before and no dirty line of the write is left for the
+step to write back.  Each call is timed with HIP events on the launch stream; the step
 time is the median over the timed steps (the minimum is reported beside it).
 
 Prints ONE JSON line: grouped-GEMM TFLOP/s (12*M*H*F per step), routed
@@ -384,11 +385,16 @@ def main():
         return
 
     # a scratch buffer larger than the MALL and all L2s, written before every
-    # step outside the timed events, so that each step starts cold
+    # step outside the timed events, so that each step starts cold; a read of a
+    # second one follows, so that the write's dirty lines are written back
+    # before the step (else the first kernel pays for that write-back)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_rd = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
 
     def evict(i):
         flush.fill_(i & 0xFF)
+        torch.sum(flush_rd, dim=0, dtype=torch.int64, out=sink)
 
     def timed_arm(arm):
         ev = {k: [] for k in ("fc1", "fc2", "dgrad")}
@@ -455,7 +461,7 @@ def main():
                    "weights": ("packed buffer (6*E*H*F bytes) + opt-in fragment-ordered copies (12*E*H*F bytes)"
                                if arms[0] == "frag" else "packed buffer (6*E*H*F bytes)")},
         "timing": "median over the timed steps of HIP-event step times on the launch stream; a 1 GiB "
-                  "scratch write before every step (outside the events) evicts the MALL and L2",
+                  "scratch write and a 1 GiB read before every step (outside the events) evict the MALL and L2",
         "ms_per_step_min": steps_min,
         "wall_ms_per_step_incl_eviction": wall_ms,
         "routed_rows_per_s": M / (ms * 1e-3), "tokens_per_s": case.T / (ms * 1e-3),
