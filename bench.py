@@ -161,26 +161,35 @@ def parity_of_sample(sample, y_gpu, dx_gpu):
     return out
 
 
-def device_record(dev):
-    """Device name, architecture, clocks (rocm-smi, if it answers) and the
-    ROCm / HIP versions."""
+def query_clocks():
+    """The device clocks as rocm-smi reports them.  Called before this process
+    initialises the GPU (a process that has must not start other programs);
+    skipped under a profiler, whose preloaded library initialises the GPU in
+    every child process."""
     import subprocess
+    if any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ):
+        return "not queried (running under a profiler)"
+    try:
+        proc = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(proc.stdout).values()))
+        return {k: v for k, v in card.items()
+                if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))}
+    except Exception as exc:   # a missing or silent rocm-smi must not fail the benchmark
+        return f"unavailable ({type(exc).__name__})"
 
+
+def device_record(dev, clocks):
+    """Device name, architecture, clocks (queried before the run) and the
+    ROCm / HIP versions."""
     import torch
     prop = torch.cuda.get_device_properties(dev)
     rec = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
-           "compute_units": prop.multi_processor_count, "hip_runtime": torch.version.hip}
+           "compute_units": prop.multi_processor_count, "hip_runtime": torch.version.hip, "clocks": clocks}
     try:
         with open("/opt/rocm/.info/version") as fh:
             rec["rocm"] = fh.read().strip()
     except OSError:
         rec["rocm"] = None
-    try:
-        proc = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        card = next(iter(json.loads(proc.stdout).values()))
-        rec["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))}
-    except Exception as exc:   # a missing or silent rocm-smi must not fail the benchmark
-        rec["clocks"] = f"unavailable ({type(exc).__name__})"
     return rec
 
 
@@ -293,6 +302,8 @@ def main():
         print("bench.py: this path runs on one GPU only (no sharding or collectives are part of it); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    clocks = query_clocks() if not args.copy_probe_mib else None   # before the GPU is initialised
 
     import numpy as np
     import torch
@@ -474,7 +485,7 @@ def main():
         "layouts": {arm: dict(r, tflops=flops / (r["ms_per_step"] * 1e-3) / 1e12) for arm, r in results.items()},
         "roofline": roof,
         "kernel_source_sha": kernel_source_hash(),
-        "device": device_record(dev),
+        "device": device_record(dev, clocks),
     }
     if not args.no_cpu_baseline:
         rec, sample = cpu_baseline(case, args.cpu_seconds, args.activation, probs_np)

@@ -1186,31 +1186,33 @@ void grouped_gemm_kernel(const GemmParams p) {
 
 // ---------------------------------------------------------------- four-wave kernel
 //
-// FC1, FC2 and dX over a fragment-ordered copy of the weights (an optional
-// buffer of the caller's, for H % 256 == 0 and F % 128 == 0), all in one launch: first
-// thin items (the at most 96 rows an expert leaves after its 256-row tiles,
-// or all rows of a small expert), then the tiles.  Four waves compute a
-// 256 x 256 tile: wave w owns token rows (w >> 1) * 128 .. +127 and weight rows
-// (w & 1) * 128 .. +127, as 4 x 4 accumulator blocks of 32 x 32 (all 256
-// AGPRs).  Tokens stream through a 4-slot LDS ring of 64-k stages by LDS-DMA,
-// three stages ahead.  Weights skip LDS: in the fragment-ordered copy the 64
-// lanes' 16-byte operands of one 32-row x 16-k block lie next to each other,
-// so every lane loads its own MFMA operand straight into VGPRs with one
-// coalesced 1 KiB load per block, seven k16 steps ahead into an 8-step
-// register ring.  Every k16 step issues the same six loads (its four weight
-// blocks seven steps ahead and two of the eight token copies of the stage
-// three stages ahead), so the number of loads issued after any one of them
-// is fixed and the waits are constant counts: a step's weights are complete
-// at vmcnt(38), a stage's token copies at vmcnt(48).  Virtual steps -12..-1
-// repeat the pattern as the prologue, and the steps past the end re-load
-// clamped addresses, so the counts hold everywhere.  The sums are the same
-// MFMA chain over k as in the eight-wave tiles and the streaming items, so a
-// row's results do not depend on which flavor computed it.
+// The four GEMMs over the caller's fragment-ordered copy of the weights (an
+// optional buffer, for H % 256 == 0 and F % 128 == 0), each in one launch:
+// first thin items (the at most 96 rows an expert leaves after its 256-row
+// tiles, or all rows of a small expert), then the tiles.  Four waves compute
+// a 256 x 256 tile: wave w owns all 256 token rows and its own 64 weight rows
+// (two 32-row blocks), as 8 x 2 accumulator blocks of 32 x 32 (all 256
+// AGPRs), so that no two waves load the same weight bytes.  Tokens stream
+// through a 4-slot LDS ring of 64-k stages by LDS-DMA, three stages ahead,
+// and each wave reads a step's eight token fragments from it.  Weights skip
+// LDS: in the fragment-ordered copy the 64 lanes' 16-byte operands of one
+// 32-row x 16-k block lie next to each other, so every lane loads its own
+// MFMA operand straight into VGPRs with one coalesced 1 KiB load per block,
+// seven k16 steps ahead into an 8-step register ring.  Every k16 step issues
+// the same four loads (its two weight blocks seven steps ahead and two of the
+// eight token copies of the stage three stages ahead), so the number of loads
+// issued after any one of them is fixed and the waits are constant counts: a
+// step's weights are complete at vmcnt(26), a stage's token copies at
+// vmcnt(32).  Virtual steps -12..-1 repeat the pattern as the prologue, and
+// the steps past the end re-load clamped addresses, so the counts hold
+// everywhere.  The sums are the same MFMA chain over k as in the eight-wave
+// tiles and the streaming items, so a row's results do not depend on which
+// flavor computed it.
 //
 // Fragment order: block b of 32 weight rows and k16 step s of an expert is
 // 512 contiguous elements; lane l's 8 are rows 32b + (l & 31), k 16s + 8(l >> 5).
 // For W1 the 32-row blocks go gate, gate, up, up per 64 features, so a wave's
-// four blocks are the gate and up rows of the same 64 features.
+// two blocks are the gate and up rows of the same 32 features.
 constexpr int T4_THREADS = 256;
 constexpr int T4_SLOT = 256 * BK;          // elements of one token stage
 constexpr int T4_NSLOT = 4;
@@ -1224,12 +1226,9 @@ __device__ __forceinline__ void wfrag_load(bf16x8& w, const uint16_t* ptr) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(w) : "v"(ptr) : "memory");
 }
 #pragma clang diagnostic pop
-// Wait for the weight fragments of the current step: at most 38 loads issued
-// after them may be outstanding.  The registers are tied to the wait so that
-// nothing reads them before it.
-__device__ __forceinline__ void wfrag_wait38(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
-    asm volatile("s_waitcnt vmcnt(38)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
-}
+// Waits for the weight fragments of the current step (at most N loads issued
+// after them may be outstanding) tie the registers they guard, so that nothing
+// reads them before the wait.
 // H1 = X W1^T over the fragment-ordered W1 (plain-store variant): the copy's
 // 32-row block b holds W1 rows gate/up of 32 features (gate, gate, up, up per
 // 64 features), so its outputs go to H1 column h1_col(b, F) onwards.
@@ -1241,8 +1240,13 @@ __device__ __forceinline__ int F_of(int N) { return N >> 1; }   // N = 2F for th
 __device__ __forceinline__ void wfrag_wait19(bf16x8& a, bf16x8& b) {
     asm volatile("s_waitcnt vmcnt(19)" : "+v"(a), "+v"(b) :: "memory");
 }
-__device__ __forceinline__ void wfrag_hold(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
-    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
+__device__ __forceinline__ void wfrag_hold2(bf16x8& a, bf16x8& b) {
+    asm volatile("" : "+v"(a), "+v"(b) :: "memory");
+}
+// A tile's step: its two weight blocks are complete at vmcnt(26) (the same
+// step's two token copies plus six steps of two loads and two copies after them).
+__device__ __forceinline__ void wfrag_wait26(bf16x8& a, bf16x8& b) {
+    asm volatile("s_waitcnt vmcnt(26)" : "+v"(a), "+v"(b) :: "memory");
 }
 
 // The plain SwiGLU derivative of four consecutive features of one token row,
@@ -1290,8 +1294,6 @@ void tile4_kernel(const GemmParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uni(tid >> 6);
-    const int wg = wave >> 1;            // token rows wg*128 .. +127
-    const int wn = wave & 1;             // weight rows wn*128 .. +127 of the tile
     const int kiters = K / BK, nsteps = K / 16;
     const int G = gridDim.x, b = blockIdx.x;
     const int slot = (G % 8 == 0) ? (b & 7) * (G >> 3) + (b >> 3) : b;
@@ -1300,9 +1302,9 @@ void tile4_kernel(const GemmParams p) {
     // logical k chunk stored there follows the [row][64 k] swizzle.
     const int lc = ((tid & 7) ^ kswz(tid >> 3)) * 8;
 
-    f32x16 acc[4][4];
-    bf16x8 wr[8][4];
-    bf16x8 tf[2][4];
+    f32x16 acc[8][2];
+    bf16x8 wr[8][2];
+    bf16x8 tf[2][8];
 
     // ---- thin items first: rows x TILE_COLS output columns.  Each wave owns
     // two 32-row weight blocks (for SwiGLU the gate and up rows of 32
@@ -1378,7 +1380,7 @@ void tile4_kernel(const GemmParams p) {
         }
         wait_vmcnt<0>();
 #pragma unroll
-        for (int s = 0; s < 8; ++s) wfrag_hold(wr[s][0], wr[s][1], wr[s][2], wr[s][3]);
+        for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
         block_barrier();
         mfma_drain();
         int opaque = 0;
@@ -1504,7 +1506,16 @@ void tile4_kernel(const GemmParams p) {
         block_barrier();   // staging reads done before the next copies land
     }
 
-    // ---- then the 256-row tiles
+    // ---- then the 256-row tiles.  Wave w owns all 256 token rows and its own
+    // 64 weight rows (two 32-row blocks: for SwiGLU the gate and up rows of 32
+    // features, else 64 output columns), as 8 x 2 accumulator blocks of
+    // 32 x 32 (all 256 AGPRs).  So no two waves load the same weight bytes:
+    // per k16 step a workgroup moves 8 KiB of weights and 8 KiB of token
+    // copies through the vector-memory path, and each wave reads the step's
+    // eight token fragments from the LDS ring.  Per k16 step every wave
+    // issues two weight loads (seven steps ahead) and two of the eight token
+    // copies of the stage three stages ahead: a step's weights are complete at
+    // vmcnt(26) (2 + 6 x 4) and a stage's token copies at vmcnt(32) (8 x 4).
     for (int t = wi - n_items; t < n_tiles; t += G) {
         const int e = uni(find_expert(s_pre, E, t));
         const int local = t - uni(s_pre[e]);
@@ -1516,10 +1527,12 @@ void tile4_kernel(const GemmParams p) {
         const int rows = min(TBM, row_end - row0);
         const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
         const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
-        // first 32-row block of this wave in fragment order
-        const int rbw = (EPI == EPI_SWIGLU) ? (col0 / 64 + wn) * 4 : (col0 + wn * 128) / 32;
+        // this wave's two 32-row blocks in fragment order (W1's blocks go gate,
+        // gate, up, up per 64 features)
+        const int wb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
+        const int wb1 = (EPI == EPI_SWIGLU) ? wb0 + 2 : wb0 + 1;
         auto wptr = [&](int g, int j) -> const uint16_t* {
-            return wfe + ((static_cast<int64_t>(rbw + j) * nsteps + g) * 64 + lane) * 8;
+            return wfe + ((static_cast<int64_t>(j ? wb1 : wb0) * nsteps + g) * 64 + lane) * 8;
         };
         // two of the eight LDS-DMA instructions of token stage s (clamped to the last)
         auto tdma = [&](int s, int part) {
@@ -1532,17 +1545,17 @@ void tile4_kernel(const GemmParams p) {
                 dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
             }
         };
-        auto rd_t = [&](int g, int buf) {
+        auto rd_t = [&](int g, int buf) {   // the eight token fragments of step g
             const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
             const int ch = 2 * (g & 3) + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(wg * 128 + i * 32 + (lane & 31), ch));
+            for (int i = 0; i < 8; ++i)
+                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
         };
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
         // prologue: virtual steps -12..-1 (weights of steps -5..6, token stages 0..2)
@@ -1550,7 +1563,7 @@ void tile4_kernel(const GemmParams p) {
         for (int g = -12; g < 0; ++g) {
             const int gw = g + 7;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wfrag_load(wr[(gw + 8) & 7][j], wptr(gw < 0 ? 0 : gw, j));
+            for (int j = 0; j < 2; ++j) wfrag_load(wr[(gw + 8) & 7][j], wptr(gw < 0 ? 0 : gw, j));
             tdma((g >> 2) + 3, g & 3);
         }
         for (int g0 = 0; g0 < nsteps; g0 += 8) {
@@ -1558,109 +1571,175 @@ void tile4_kernel(const GemmParams p) {
             for (int u = 0; u < 8; ++u) {
                 const int g = g0 + u;
                 const int j4 = u & 3;
+                // each step's instructions stay in their step: the MFMAs of a
+                // stage's last step are issued before the next stage's barrier
+                __builtin_amdgcn_sched_barrier(0);
                 if (j4 == 0) {
-                    wait_vmcnt<48>();    // this wave's copies of stage g / 4
+                    wait_vmcnt<32>();    // this wave's copies of stage g / 4
                     block_barrier();     // everyone's; slot (g / 4 - 1) % 4 is free again
                     rd_t(g, u & 1);
                 }
                 if (j4 < 3) rd_t(g + 1, (u + 1) & 1);
-                wfrag_wait38(wr[u][0], wr[u][1], wr[u][2], wr[u][3]);
+                wfrag_wait26(wr[u][0], wr[u][1]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 2; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
                 const int gw = g + 7;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
+                for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
                 tdma((g >> 2) + 3, j4);
             }
         }
         // drain the clamped loads; the ring becomes the epilogue's staging area
         wait_vmcnt<0>();
 #pragma unroll
-        for (int s = 0; s < 8; ++s) wfrag_hold(wr[s][0], wr[s][1], wr[s][2], wr[s][3]);
+        for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
         block_barrier();
         mfma_drain();
+        // Values derived below are computed here, not hoisted above the K loop.
         int opaque = 0;
         asm volatile("" : "+s"(opaque));
-        const int wrow0 = row0 + wg * 128 + opaque;    // first token row of this wave
+        const int trow0 = row0 + opaque;
+        const int ln = lane + opaque;
         uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
+        // Lane holds token row (ln & 31) of each token block i and, for
+        // register 4q + x of block j, weight row 32j + 8q + 4(ln >> 5) + x of
+        // the wave's 64.
         if constexpr (EPI == EPI_STORE) {
-            // [128 rows][128 cols] bf16; 16-byte chunk c of row r at c ^ (r & 15)
+            // [256 rows][64 cols] bf16 (128-byte rows); 16-byte chunk c of row r at c ^ (r & 7)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int r = i * 32 + (lane & 31);
+                        const int r = i * 32 + (ln & 31);
                         const int c = j * 4 + q;
                         uint2 v;
                         v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
                         v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
-                        *reinterpret_cast<uint2*>(stg + r * 128 + ((c ^ (r & 15)) << 3) + 4 * (lane >> 5)) = v;
+                        *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (ln >> 5)) = v;
                     }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const int gcol0 = col0 + wn * 128;
+            const int gcol0 = col0 + 64 * wave;
 #pragma unroll 4
             for (int sidx = 0; sidx < 32; ++sidx) {
-                const int idx = sidx * 64 + lane;
-                const int r = idx >> 4, c = idx & 15;
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + ((c ^ (r & 15)) << 3));
-                const int oc = p.h1_order ? h1_col(rbw + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
-                if (wrow0 + r < row_end)
-                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(wrow0 + r) * N + oc) = v;
+                const int idx = sidx * 64 + ln;
+                const int r = idx >> 3, pc = idx & 7;
+                const int c = pc ^ (r & 7);
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + pc * 8);
+                const int oc = p.h1_order ? h1_col(wb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
+                if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
             }
-        } else if constexpr (EPI == EPI_DSWIGLU) {
-            // SwiGLU derivative.  Per pass of 32 token rows (token block i) the
-            // saved gate and up values of the wave's 128 features,
-            // [32 rows][gate 128 | up 128] bf16 (512-byte rows, 16 KiB), are
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            // two passes of 128 token rows; per pass [128][32] bf16 arrays for
+            // A, gate and up (64-byte rows); 16-byte chunk c of row r at c ^ (r & 3)
+            uint16_t* sA = stg;
+            uint16_t* sG = stg + 4096;
+            uint16_t* sU = stg + 8192;
+            const int fcol0 = col0 + 32 * wave;        // first feature of this wave
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int i = pass * 4 + ii;
+                    const int r = ii * 32 + (ln & 31);
+                    const int prow = trow0 + pass * 128 + r;
+                    const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (ln >> 5);
+                        uint32_t gb[4], ub[4], ab[4];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
+                            ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
+                            const float gv = bf2f(gb[x]);
+                            const float uv = bf2f(ub[x]);
+                            const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
+                            const float v = sg * uv;
+                            ab[x] = f2bf(probs ? pr * v : v);
+                        }
+                        *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                        *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
+                        *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+                for (int sidx = 0; sidx < 8; ++sidx) {
+                    const int idx = sidx * 64 + ln;
+                    const int r = idx >> 2, pc = idx & 3;
+                    const int c = pc ^ (r & 3);
+                    const int off = r * 32 + pc * 8;
+                    const int grow = trow0 + pass * 128 + r;
+                    const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
+                    const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                    const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                    if (grow < row_end) {
+                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + fcol0 + c * 8) = va;
+                        if (p.out1) {
+                            uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + fcol0 + c * 8;
+                            *reinterpret_cast<uint4*>(h) = vg;
+                            *reinterpret_cast<uint4*>(h + N) = vu;
+                        }
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        } else {
+            // SwiGLU derivative.  Per pass of 64 token rows (token blocks 2p,
+            // 2p + 1) the saved gate and up values of the wave's 64 features,
+            // [64 rows][gate 64 | up 64] bf16 (256-byte rows, 16 KiB), are
             // copied into one of two staging buffers with LDS-DMA (rows past
-            // the tile repeat its last row); 16-byte chunk c (0..15 gate, 16..31
-            // up) of row r sits at (c & 16) | ((c & 15) ^ (r & 15)).  The next
+            // the tile repeat its last row); 16-byte chunk c (0..7 gate, 8..15
+            // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The next
             // pass's copy is in flight while a pass is computed in place and
             // stored as whole row segments of dH1.  The waits count this wave's
             // memory operations in issue order: 16 copies or 16 stores a pass.
             const int F = N;
-            const int f0 = col0 + wn * 128 + opaque;
-            const int ln = lane + opaque;     // per-lane values computed here, not above the K loop
+            const int f0 = col0 + 64 * wave + opaque;
             const int trows = rows + opaque;
             const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
             const uint32_t sl = lds_addr(stg);
             auto h1_copy = [&](int pass, int buf) {
 #pragma unroll
                 for (int d = 0; d < 16; ++d) {
-                    const int r = 2 * d + (ln >> 5), pc = ln & 31;
-                    const int c = (pc & 16) | ((pc & 15) ^ (r & 15));
-                    const int trow = min(wg * 128 + pass * 32 + r, trows - 1);
-                    const int col = (c < 16 ? 0 : F) + f0 + 8 * (c & 15);
+                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                    const int trow = min(pass * 64 + r, trows - 1);
+                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
                     dma16(hb, static_cast<uint32_t>((trow * 2 * F + col) * 2), sl + buf * 16384 + d * 1024);
                 }
             };
             auto h1_compute = [&](auto pass_tag, int buf) {
-                constexpr int i = decltype(pass_tag)::value;
-                const int r = ln & 31;
-                uint16_t* b = stg + buf * 8192;
+                constexpr int pass = decltype(pass_tag)::value;
+                uint16_t* bb = stg + buf * 8192;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int r = ii * 32 + (ln & 31);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int pos = (4 * j + q) ^ (r & 15);
-                        uint16_t* pg = b + r * 256 + pos * 8 + 4 * (ln >> 5);
-                        dswiglu_inplace(pg, pg + 128, acc[i][j], q);
-                    }
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int pos = (4 * j + q) ^ (r & 7);
+                            uint16_t* pg = bb + r * 128 + pos * 8 + 4 * (ln >> 5);
+                            dswiglu_inplace(pg, pg + 64, acc[2 * pass + ii][j], q);
+                        }
+                }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             };
             auto h1_store = [&](int pass, int buf) {
-                const uint16_t* b = stg + buf * 8192;
+                const uint16_t* bb = stg + buf * 8192;
 #pragma unroll
                 for (int d = 0; d < 16; ++d) {
-                    const int r = 2 * d + (ln >> 5), pc = ln & 31;
-                    const int c = (pc & 16) | ((pc & 15) ^ (r & 15));
-                    const uint4 v = *reinterpret_cast<const uint4*>(b + r * 256 + pc * 8);
-                    const int grow = wrow0 + pass * 32 + r;
-                    const int col = (c < 16 ? 0 : F) + f0 + 8 * (c & 15);
+                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                    const uint4 v = *reinterpret_cast<const uint4*>(bb + r * 128 + pc * 8);
+                    const int grow = trow0 + pass * 64 + r;
+                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
                     if (grow < row_end) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * (2 * F) + col) = v;
                 }
                 // the buffer's reads are done before a copy refills it
@@ -1682,68 +1761,11 @@ void tile4_kernel(const GemmParams p) {
             wait_vmcnt<16>();                       // pass 3
             h1_compute(GrpTag<3>{}, 1);
             h1_store(3, 1);
-        } else {
-            // per pass of 64 token rows, [64][64] bf16 arrays for A, gate and up;
-            // 16-byte chunk c of row r at c ^ (r & 7)
-            uint16_t* sA = stg;
-            uint16_t* sG = stg + 4096;
-            uint16_t* sU = stg + 8192;
-            const int fcol0 = col0 + wn * 64;          // first feature of this wave
-#pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = pass * 2 + ii;
-                    const int r = ii * 32 + (lane & 31);
-                    const int prow = wrow0 + pass * 64 + r;
-                    const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int c = jj * 4 + q;
-                            const int off = r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5);
-                            uint32_t gb[4], ub[4], ab[4];
-#pragma unroll
-                            for (int x = 0; x < 4; ++x) {
-                                gb[x] = f2bf(acc_rd(acc[i][jj][q * 4 + x]));
-                                ub[x] = f2bf(acc_rd(acc[i][2 + jj][q * 4 + x]));
-                                const float gv = bf2f(gb[x]);
-                                const float uv = bf2f(ub[x]);
-                                const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
-                                const float v = sg * uv;
-                                ab[x] = f2bf(probs ? pr * v : v);
-                            }
-                            *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                            *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                            *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
-                        }
-                }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll 2
-                for (int sidx = 0; sidx < 8; ++sidx) {
-                    const int idx = sidx * 64 + lane;
-                    const int r = idx >> 3, c = idx & 7;
-                    const int off = r * 64 + ((c ^ (r & 7)) << 3);
-                    const int grow = wrow0 + pass * 64 + r;
-                    const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
-                    const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
-                    const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
-                    if (grow < row_end) {
-                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + fcol0 + c * 8) = va;
-                        if (p.out1) {
-                            uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + fcol0 + c * 8;
-                            *reinterpret_cast<uint4*>(h) = vg;
-                            *reinterpret_cast<uint4*>(h + N) = vu;
-                        }
-                    }
-                }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            }
         }
         block_barrier();   // staging reads done before the next tile's copies land
     }
 }
+
 
 // Fragment-ordered copies (layout above) of every expert's W1 and W2 for the
 // forward tiles, of W1^T [H][2F] for dX = dH1 W1 and of W2^T [F][H] for
