@@ -1198,16 +1198,18 @@ void grouped_gemm_kernel(const GemmParams p) {
 // LDS: in the fragment-ordered copy the 64 lanes' 16-byte operands of one
 // 32-row x 16-k block lie next to each other, so every lane loads its own
 // MFMA operand straight into VGPRs with one coalesced 1 KiB load per block,
-// seven k16 steps ahead into an 8-step register ring.  Every k16 step issues
-// the same four loads (its two weight blocks seven steps ahead and two of the
-// eight token copies of the stage three stages ahead), so the number of loads
-// issued after any one of them is fixed and the waits are constant counts: a
-// step's weights are complete at vmcnt(26), a stage's token copies at
-// vmcnt(32).  Virtual steps -12..-1 repeat the pattern as the prologue, and
-// the steps past the end re-load clamped addresses, so the counts hold
-// everywhere.  The sums are the same MFMA chain over k as in the eight-wave
-// tiles and the streaming items, so a row's results do not depend on which
-// flavor computed it.
+// seven k16 steps ahead into an 8-step register ring.  Every k16 step of a
+// tile issues the same four loads (its two weight blocks seven steps ahead
+// and two of the eight token copies of a stage three stages ahead; a thin
+// item's step one copy of four), so the number of loads issued after any one
+// of them is fixed and the waits are constant counts: a tile step's weights
+// are complete at vmcnt(26) and a thin item's at vmcnt(19); a thin item's
+// stage copies are complete at vmcnt(24), and in tiles the weight wait of a
+// stage's last step already covers the next stage's copies.  Virtual steps
+// before step 0 repeat the pattern as the prologue, and the steps past the
+// end re-load clamped addresses, so the counts hold everywhere.  The sums are
+// the same MFMA chain over k as in the eight-wave tiles and the streaming
+// items, so a row's results do not depend on which flavor computed it.
 //
 // Fragment order: block b of 32 weight rows and k16 step s of an expert is
 // 512 contiguous elements; lane l's 8 are rows 32b + (l & 31), k 16s + 8(l >> 5).
@@ -1512,10 +1514,15 @@ void tile4_kernel(const GemmParams p) {
     // 32 x 32 (all 256 AGPRs).  So no two waves load the same weight bytes:
     // per k16 step a workgroup moves 8 KiB of weights and 8 KiB of token
     // copies through the vector-memory path, and each wave reads the step's
-    // eight token fragments from the LDS ring.  Per k16 step every wave
-    // issues two weight loads (seven steps ahead) and two of the eight token
-    // copies of the stage three stages ahead: a step's weights are complete at
-    // vmcnt(26) (2 + 6 x 4) and a stage's token copies at vmcnt(32) (8 x 4).
+    // eight token fragments from the LDS ring, one step ahead.  Per k16 step
+    // every wave issues two weight loads (seven steps ahead) and two of the
+    // eight token copies of a stage three stages ahead: stage s + 4 in steps
+    // 4s + 3 .. 4s + 6, after the barrier of step 4s + 3 (the last of stage s)
+    // has freed slot s % 4.  A step's weights are complete at vmcnt(26)
+    // (2 + 6 x 4), and that wait in step 4s + 3 also covers this wave's
+    // copies of stage s + 1, the last of which has 28 loads after it; so the
+    // barrier there lets every wave read the first fragments of stage s + 1
+    // a step ahead like all others.
     for (int t = wi - n_items; t < n_tiles; t += G) {
         const int e = uni(find_expert(s_pre, E, t));
         const int local = t - uni(s_pre[e]);
@@ -1558,29 +1565,36 @@ void tile4_kernel(const GemmParams p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-        // prologue: virtual steps -12..-1 (weights of steps -5..6, token stages 0..2)
+        // prologue: virtual steps -13..-1 (weights of steps -6..6, token stages
+        // 0..2 and the first copy of stage 3); step -1 ends like the last step
+        // of a stage: stage 0 is in, and its first step's fragments are read
 #pragma unroll
-        for (int g = -12; g < 0; ++g) {
+        for (int g = -13; g < 0; ++g) {
             const int gw = g + 7;
+            if (g == -1) {
+                wait_vmcnt<32>();    // this wave's copies of stage 0
+                block_barrier();
+                rd_t(0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) wfrag_load(wr[(gw + 8) & 7][j], wptr(gw < 0 ? 0 : gw, j));
-            tdma((g >> 2) + 3, g & 3);
+            tdma(((g + 1) >> 2) + 3, (g + 1) & 3);
         }
         for (int g0 = 0; g0 < nsteps; g0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int g = g0 + u;
                 const int j4 = u & 3;
-                // each step's instructions stay in their step: the MFMAs of a
-                // stage's last step are issued before the next stage's barrier
+                // each step's instructions stay in their step
                 __builtin_amdgcn_sched_barrier(0);
-                if (j4 == 0) {
-                    wait_vmcnt<32>();    // this wave's copies of stage g / 4
-                    block_barrier();     // everyone's; slot (g / 4 - 1) % 4 is free again
-                    rd_t(g, u & 1);
-                }
-                if (j4 < 3) rd_t(g + 1, (u + 1) & 1);
+                // this step's weights; in a stage's last step also this wave's
+                // copies of the next stage (28 loads were issued after them)
                 wfrag_wait26(wr[u][0], wr[u][1]);
+                // In a stage's last step: every wave's copies of the next
+                // stage are in, and every wave has read all of this stage's
+                // fragments, so its slot may be refilled from here on.
+                if (j4 == 3) block_barrier();
+                rd_t(g + 1, (u + 1) & 1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1589,7 +1603,16 @@ void tile4_kernel(const GemmParams p) {
                 const int gw = g + 7;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
-                tdma((g >> 2) + 3, j4);
+                tdma(((g + 1) >> 2) + 3, (j4 + 1) & 3);
+                // issue order within the step: one token fragment read for the
+                // next step after each of the first eight MFMAs, so the reads
+                // spread over the step instead of bunching behind its MFMAs
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             }
         }
         // drain the clamped loads; the ring becomes the epilogue's staging area
