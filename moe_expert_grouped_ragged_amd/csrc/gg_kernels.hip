@@ -1227,6 +1227,20 @@ constexpr int T4_NSLOT = 4;
 __device__ __forceinline__ void wfrag_load(bf16x8& w, const uint16_t* ptr) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(w) : "v"(ptr) : "memory");
 }
+// The same load under a wave-uniform lane mask (all lanes, or lane 0 alone
+// for a load whose data is not used): it is issued and counted like any
+// other, but moves 16 bytes instead of 1 KiB.  The mask is set for this one
+// instruction inside the asm block.
+__device__ __forceinline__ void wfrag_load_m(bf16x8& w, const uint16_t* ptr, uint64_t mask) {
+    uint64_t saved;
+    asm volatile("s_mov_b64 %1, exec\n\t"
+                 "s_mov_b64 exec, %3\n\t"
+                 "global_load_dwordx4 %0, %2, off\n\t"
+                 "s_mov_b64 exec, %1"
+                 : "+v"(w), "=&s"(saved)
+                 : "v"(ptr), "s"(mask)
+                 : "memory");
+}
 #pragma clang diagnostic pop
 // Waits for the weight fragments of the current step (at most N loads issued
 // after them may be outstanding) tie the registers they guard, so that nothing
@@ -1315,10 +1329,24 @@ void tile4_kernel(const GemmParams p) {
     // three stages ahead (128 rows, the ones past the item clamped), so a
     // step's weights are complete at vmcnt(19) and a stage's tokens at
     // vmcnt(24).
+    //   A thin item is bound by the bytes its workgroup moves.  When the
+    // thin items fit into the grid twice over, each is split into two halves
+    // of its columns, so twice as many workgroups share its weight bytes.
+    // A half keeps the loop as it is: for plain stores each wave owns one
+    // 32-row block (its second load and MFMAs repeat the first); for SwiGLU
+    // waves 0 and 1 own the gate and up blocks of the half's 32 + 32
+    // features and waves 2 and 3 repeat them.  The repeated loads run on one
+    // lane, the repeated results are not stored, and a row's arithmetic is
+    // the same either way.
+    constexpr bool THIN_HALVES = EPI != EPI_DSWIGLU;
+    const int h_sh = (THIN_HALVES && 2 * n_items <= G) ? 1 : 0;   // log2 of the work units per thin item
+    const int n_units = n_items << h_sh;
     int wi = slot;
-    for (; wi < n_items; wi += G) {
-        const int e = uni(find_expert(s_spre, E, wi));
-        const int local = wi - uni(s_spre[e]);
+    for (; wi < n_units; wi += G) {
+        const int ti = wi >> h_sh;     // thin item
+        const int hf = wi & h_sh;      // its half (0 for a whole item)
+        const int e = uni(find_expert(s_spre, E, ti));
+        const int local = ti - uni(s_spre[e]);
         const int rb = uni(s_off[e]);
         const int re = uni(s_off[e + 1]);
         const int row0 = uni(rb + tile_rows_of(re - rb));
@@ -1326,8 +1354,14 @@ void tile4_kernel(const GemmParams p) {
         const int col0 = uni(local * TILE_COLS);
         const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
         const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
-        const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
-        const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : tb0 + 1;
+        const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (h_sh ? hf : (wave >> 1))) * 4 + (wave & 1)
+                                            : col0 / 32 + (h_sh ? 4 * hf + wave : 2 * wave);
+        const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : (h_sh ? tb0 : tb0 + 1);
+        // loads whose results a half item does not store move one lane only
+        const bool rep0 = h_sh && EPI == EPI_SWIGLU && wave >= 2;
+        const bool rep1 = h_sh && (EPI != EPI_SWIGLU || wave >= 2);
+        const uint64_t lm0 = uni(rep0) ? 1ull : ~0ull;
+        const uint64_t lm1 = uni(rep1) ? 1ull : ~0ull;
         auto wp = [&](int g, int j) -> const uint16_t* {
             return wfe + ((static_cast<int64_t>(j ? tb1 : tb0) * nsteps + g) * 64 + lane) * 8;
         };
@@ -1354,7 +1388,7 @@ void tile4_kernel(const GemmParams p) {
         for (int g = -12; g < 0; ++g) {
             const int gw = g + 7;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) wfrag_load(wr[(gw + 8) & 7][j], wp(gw < 0 ? 0 : gw, j));
+            for (int j = 0; j < 2; ++j) wfrag_load_m(wr[(gw + 8) & 7][j], wp(gw < 0 ? 0 : gw, j), j ? lm1 : lm0);
             tdma1((g >> 2) + 3, g & 3);
         }
         for (int g0 = 0; g0 < nsteps; g0 += 8) {
@@ -1376,7 +1410,8 @@ void tile4_kernel(const GemmParams p) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
                 const int gw = g + 7;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j));
+                for (int j = 0; j < 2; ++j)
+                    wfrag_load_m(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j), j ? lm1 : lm0);
                 tdma1((g >> 2) + 3, j4);
             }
         }
@@ -1405,14 +1440,15 @@ void tile4_kernel(const GemmParams p) {
                         *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5)) = v;
                     }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const int gcol0 = col0 + 64 * wave;
+            // a half item's wave stores its first 32 columns (block tb0) only
+            const int gcol0 = col0 + (h_sh ? 128 * hf + 32 * wave : 64 * wave);
 #pragma unroll 4
             for (int sidx = 0; sidx < 12; ++sidx) {
                 const int idx = sidx * 64 + lane;
                 const int r = idx >> 3, c = idx & 7;
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (r & 7)) << 3));
                 const int oc = p.h1_order ? h1_col(tb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
-                if (r < rows)
+                if (r < rows && (!h_sh || c < 4))
                     *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
             }
         } else if constexpr (EPI == EPI_DSWIGLU) {
@@ -1462,7 +1498,9 @@ void tile4_kernel(const GemmParams p) {
             uint16_t* sA = stg;
             uint16_t* sG = stg + 3072;
             uint16_t* sU = stg + 6144;
-            const int fcol0 = col0 + 32 * wave;
+            // a half item's features are stored by waves 0 and 1
+            const int fcol0 = col0 + (h_sh ? 64 * hf : 0) + 32 * wave;
+            const bool owns = !h_sh || wave < 2;
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 const int r = i * 32 + (lane & 31);
@@ -1495,7 +1533,7 @@ void tile4_kernel(const GemmParams p) {
                 const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
                 const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
                 const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
-                if (r < rows) {
+                if (r < rows && owns) {
                     *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + fcol0 + c * 8) = va;
                     if (p.out1) {
                         uint16_t* h = p.out1 + static_cast<int64_t>(trow0 + r) * (2 * N) + fcol0 + c * 8;
@@ -1523,7 +1561,7 @@ void tile4_kernel(const GemmParams p) {
     // copies of stage s + 1, the last of which has 28 loads after it; so the
     // barrier there lets every wave read the first fragments of stage s + 1
     // a step ahead like all others.
-    for (int t = wi - n_items; t < n_tiles; t += G) {
+    for (int t = wi - n_units; t < n_tiles; t += G) {
         const int e = uni(find_expert(s_pre, E, t));
         const int local = t - uni(s_pre[e]);
         const int rb = uni(s_off[e]);
