@@ -78,9 +78,17 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ float bf2f(uint32_t b16) {
     return __builtin_bit_cast(float, b16 << 16);
 }
+// Two floats rounded to bf16 (round to nearest even, as f2bf) and packed,
+// lo in bits 0..15: one v_cvt_pk_bf16_f32 for the pair.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+// The two bf16 values of a packed pair as floats.
+__device__ __forceinline__ float lo_f(uint32_t pr) { return __builtin_bit_cast(float, pr << 16); }
+__device__ __forceinline__ float hi_f(uint32_t pr) { return __builtin_bit_cast(float, pr & 0xffff0000u); }
 
 // Chunk swizzles (chosen from LDS bank-conflict counter measurements on
 // gfx950).  K-contiguous panels are [row][64 k] (128-byte rows, eight 16-byte
@@ -160,6 +168,32 @@ __device__ __forceinline__ float acc_rd(float a) {
     float v;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
     return v;
+}
+// SwiGLU of four outputs: gate and up accumulators q*4 .. q*4+3 of ga and
+// ua, each rounded to bf16, then a = bf16(p * (g * sigmoid(slope * g) * u))
+// (p = 1 without probabilities).  Returns the bf16 A, gate and up values as
+// two packed pairs each.
+__device__ __forceinline__ void swiglu4(const f32x16& ga, const f32x16& ua, int q, float slope, float pr,
+                                        bool weighted, uint2& a_out, uint2& g_out, uint2& u_out) {
+    uint32_t gp[2], up[2], ap[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        gp[h] = pack2(acc_rd(ga[q * 4 + 2 * h]), acc_rd(ga[q * 4 + 2 * h + 1]));
+        up[h] = pack2(acc_rd(ua[q * 4 + 2 * h]), acc_rd(ua[q * 4 + 2 * h + 1]));
+        float av[2];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const float g = y ? hi_f(gp[h]) : lo_f(gp[h]);
+            const float u = y ? hi_f(up[h]) : lo_f(up[h]);
+            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
+            const float v = sg * u;
+            av[y] = weighted ? pr * v : v;
+        }
+        ap[h] = pack2(av[0], av[1]);
+    }
+    a_out = make_uint2(ap[0], ap[1]);
+    g_out = make_uint2(gp[0], gp[1]);
+    u_out = make_uint2(up[0], up[1]);
 }
 
 template <typename T>
@@ -741,20 +775,25 @@ void grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
                         for (int g = 0; g < 2; ++g) {
                             const int fl = wave * 16 + 8 * g + 4 * (lane >> 5);
-                            uint32_t gb[4], ub[4], ab[4];
+                            uint32_t gp[2], up[2], ap[2];   // bf16 pairs
 #pragma unroll
-                            for (int x = 0; x < 4; ++x) {
-                                gb[x] = f2bf(acc_rd(sacc[b][4 * g + x]));
-                                ub[x] = f2bf(acc_rd(sacc[b][4 * g + 8 + x]));
-                                const float gg = bf2f(gb[x]);
-                                const float uu = bf2f(ub[x]);
-                                const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
-                                ab[x] = f2bf(probs ? pr * v : v);
+                            for (int h = 0; h < 2; ++h) {
+                                gp[h] = pack2(acc_rd(sacc[b][4 * g + 2 * h]), acc_rd(sacc[b][4 * g + 2 * h + 1]));
+                                up[h] = pack2(acc_rd(sacc[b][4 * g + 8 + 2 * h]), acc_rd(sacc[b][4 * g + 8 + 2 * h + 1]));
+                                float av[2];
+#pragma unroll
+                                for (int y = 0; y < 2; ++y) {
+                                    const float gg = y ? hi_f(gp[h]) : lo_f(gp[h]);
+                                    const float uu = y ? hi_f(up[h]) : lo_f(up[h]);
+                                    const float v = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg))) * uu;
+                                    av[y] = probs ? pr * v : v;
+                                }
+                                ap[h] = pack2(av[0], av[1]);
                             }
                             uint16_t* sr = stg + r * SLD + fl;
-                            *reinterpret_cast<uint2*>(sr) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                            *reinterpret_cast<uint2*>(sr + S_COLS) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                            *reinterpret_cast<uint2*>(sr + 2 * S_COLS) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                            *reinterpret_cast<uint2*>(sr) = make_uint2(ap[0], ap[1]);
+                            *reinterpret_cast<uint2*>(sr + S_COLS) = make_uint2(gp[0], gp[1]);
+                            *reinterpret_cast<uint2*>(sr + 2 * S_COLS) = make_uint2(up[0], up[1]);
                         }
                     } else {
                         const float pr = (probs && rv) ? probs[grow] : 1.0f;
@@ -768,12 +807,14 @@ void grouped_gemm_kernel(const GemmParams p) {
                             const uint2 hu = *reinterpret_cast<const uint2*>(sg + S_COLS);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
+                            const uint32_t dw[2] = {pack2(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
+                                                    pack2(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3]))};
                             float dg[4], du[4];
 #pragma unroll
                             for (int x = 0; x < 4; ++x) {
-                                const float gg = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
-                                const float uu = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
-                                const float da = bf2f(f2bf(acc_rd(sacc[b][4 * g + x])));
+                                const float gg = (x & 1) ? hi_f(gw[x >> 1]) : lo_f(gw[x >> 1]);
+                                const float uu = (x & 1) ? hi_f(uw[x >> 1]) : lo_f(uw[x >> 1]);
+                                const float da = (x & 1) ? hi_f(dw[x >> 1]) : lo_f(dw[x >> 1]);
                                 const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gg)));
                                 const float dap = probs ? pr * da : da;
                                 dg[x] = dap * uu * sgm * (1.0f + slope * gg * (1.0f - sgm));
@@ -1039,20 +1080,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                         const int r = ii * 32 + (lane & 31);
                         const int u = q * 2 + (lane >> 5);
                         const int off = r * 32 + ((u ^ ((r >> 2) & 7)) << 2);
-                        uint32_t gb[4], ub[4], ab[4];
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
-                            ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
-                            const float g = bf2f(gb[x]);
-                            const float uu = bf2f(ub[x]);
-                            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
-                            const float v = sg * uu;
-                            ab[x] = f2bf(probs ? pr * v : v);
-                        }
-                        *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                        *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                        *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                        swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr, *reinterpret_cast<uint2*>(sA + off),
+                                *reinterpret_cast<uint2*>(sG + off), *reinterpret_cast<uint2*>(sU + off));
                     }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1128,14 +1157,14 @@ void grouped_gemm_kernel(const GemmParams p) {
                             const uint2 hu = *reinterpret_cast<const uint2*>(sU + off);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
+                            const uint32_t dw[2] = {pack2(acc_rd(acc[i][j][q * 4]), acc_rd(acc[i][j][q * 4 + 1])),
+                                                    pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]))};
                             float dg[4], du[4];
 #pragma unroll
                             for (int x = 0; x < 4; ++x) {
-                                const uint32_t gbits = (x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu);
-                                const uint32_t ubits = (x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu);
-                                const float g = bf2f(gbits);
-                                const float u = bf2f(ubits);
-                                const float da = bf2f(f2bf(acc_rd(acc[i][j][q * 4 + x])));
+                                const float g = (x & 1) ? hi_f(gw[x >> 1]) : lo_f(gw[x >> 1]);
+                                const float u = (x & 1) ? hi_f(uw[x >> 1]) : lo_f(uw[x >> 1]);
+                                const float da = (x & 1) ? hi_f(dw[x >> 1]) : lo_f(dw[x >> 1]);
                                 const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
                                 const float dap = probs ? pr * da : da;
                                 dg[x] = dap * u * sgm * (1.0f + slope * g * (1.0f - sgm));
@@ -1274,12 +1303,13 @@ __device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, cons
     const uint2 hu = *reinterpret_cast<const uint2*>(pu);
     const uint32_t gw[2] = {hg.x, hg.y};
     const uint32_t uw[2] = {hu.x, hu.y};
+    const uint32_t dw[2] = {pack2(acc_rd(a[q * 4]), acc_rd(a[q * 4 + 1])), pack2(acc_rd(a[q * 4 + 2]), acc_rd(a[q * 4 + 3]))};
     float dg[4], du[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-        const float g = bf2f((x & 1) ? (gw[x >> 1] >> 16) : (gw[x >> 1] & 0xffffu));
-        const float u = bf2f((x & 1) ? (uw[x >> 1] >> 16) : (uw[x >> 1] & 0xffffu));
-        const float da = bf2f(f2bf(acc_rd(a[q * 4 + x])));
+        const float g = (x & 1) ? hi_f(gw[x >> 1]) : lo_f(gw[x >> 1]);
+        const float u = (x & 1) ? hi_f(uw[x >> 1]) : lo_f(uw[x >> 1]);
+        const float da = (x & 1) ? hi_f(dw[x >> 1]) : lo_f(dw[x >> 1]);
         const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(1.0f * g)));
         dg[x] = da * u * sgm * (1.0f + 1.0f * g * (1.0f - sgm));
         du[x] = da * g * sgm;
@@ -1508,20 +1538,8 @@ void tile4_kernel(const GemmParams p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (lane >> 5);
-                    uint32_t gb[4], ub[4], ab[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
-                        ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
-                        const float gv = bf2f(gb[x]);
-                        const float uv = bf2f(ub[x]);
-                        const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
-                        const float v = sg * uv;
-                        ab[x] = f2bf(probs ? pr * v : v);
-                    }
-                    *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                    *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                    *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                    swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr, *reinterpret_cast<uint2*>(sA + off),
+                            *reinterpret_cast<uint2*>(sG + off), *reinterpret_cast<uint2*>(sU + off));
                 }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1712,20 +1730,8 @@ void tile4_kernel(const GemmParams p) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (ln >> 5);
-                        uint32_t gb[4], ub[4], ab[4];
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            gb[x] = f2bf(acc_rd(acc[i][0][q * 4 + x]));
-                            ub[x] = f2bf(acc_rd(acc[i][1][q * 4 + x]));
-                            const float gv = bf2f(gb[x]);
-                            const float uv = bf2f(ub[x]);
-                            const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * gv)));
-                            const float v = sg * uv;
-                            ab[x] = f2bf(probs ? pr * v : v);
-                        }
-                        *reinterpret_cast<uint2*>(sA + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                        *reinterpret_cast<uint2*>(sG + off) = make_uint2(gb[0] | (gb[1] << 16), gb[2] | (gb[3] << 16));
-                        *reinterpret_cast<uint2*>(sU + off) = make_uint2(ub[0] | (ub[1] << 16), ub[2] | (ub[3] << 16));
+                        swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr, *reinterpret_cast<uint2*>(sA + off),
+                                *reinterpret_cast<uint2*>(sG + off), *reinterpret_cast<uint2*>(sU + off));
                     }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
