@@ -1641,8 +1641,6 @@ void tile4_kernel(const GemmParams p) {
             for (int u = 0; u < 8; ++u) {
                 const int g = g0 + u;
                 const int j4 = u & 3;
-                // each step's instructions stay in their step
-                __builtin_amdgcn_sched_barrier(0);
                 // this step's weights; in a stage's last step also this wave's
                 // copies of the next stage (28 loads were issued after them)
                 wfrag_wait26(wr[u][0], wr[u][1]);
