@@ -86,6 +86,12 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+// The same bits from two separate conversions.  Only one float is live at a
+// time, which suits kernels short of registers (the eight-wave dgrad
+// instances measured about 5% slower with the paired form).
+__device__ __forceinline__ uint32_t pack2_sep(float lo, float hi) {
+    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
 // The two bf16 values of a packed pair as floats.
 __device__ __forceinline__ float lo_f(uint32_t pr) { return __builtin_bit_cast(float, pr << 16); }
 __device__ __forceinline__ float hi_f(uint32_t pr) { return __builtin_bit_cast(float, pr & 0xffff0000u); }
@@ -308,6 +314,12 @@ constexpr int LDS_BUF_EL = S_RING_EL > NSTAGE * (A_STAGE + B_STAGE) ? S_RING_EL 
 template <bool W_KN, int EPI, bool EXT>
 __global__ __launch_bounds__(NTHREADS)
 void grouped_gemm_kernel(const GemmParams p) {
+    // bf16 pair packing for the epilogues: separate conversions in the dgrad
+    // instances (transposed weights), which are short of registers
+    auto pk = [](float lo, float hi) -> uint32_t {
+        if constexpr (W_KN) return pack2_sep(lo, hi);
+        else return pack2(lo, hi);
+    };
     const float slope = EXT ? p.slope : 1.0f;
     const float* const probs = EXT ? p.probs : nullptr;
     float* const dp_part = EXT ? p.dp_part : nullptr;
@@ -767,8 +779,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                         for (int g = 0; g < 4; ++g) {
                             const int cl = wave * 32 + 8 * g + 4 * (lane >> 5);
                             *reinterpret_cast<uint2*>(stg + r * SLD + cl) =
-                                make_uint2(pack2(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
-                                           pack2(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3])));
+                                make_uint2(pk(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
+                                           pk(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3])));
                         }
                     } else if constexpr (EPI == EPI_SWIGLU) {
                         const float pr = (probs && rv) ? probs[grow] : 1.0f;
@@ -807,8 +819,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                             const uint2 hu = *reinterpret_cast<const uint2*>(sg + S_COLS);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
-                            const uint32_t dw[2] = {pack2(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
-                                                    pack2(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3]))};
+                            const uint32_t dw[2] = {pk(acc_rd(sacc[b][4 * g]), acc_rd(sacc[b][4 * g + 1])),
+                                                    pk(acc_rd(sacc[b][4 * g + 2]), acc_rd(sacc[b][4 * g + 3]))};
                             float dg[4], du[4];
 #pragma unroll
                             for (int x = 0; x < 4; ++x) {
@@ -821,8 +833,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 du[x] = dap * gg * sgm;
                                 if (fv) dps += da * (gg * sgm * uu);
                             }
-                            *reinterpret_cast<uint2*>(sg) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
-                            *reinterpret_cast<uint2*>(sg + S_COLS) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+                            *reinterpret_cast<uint2*>(sg) = make_uint2(pk(dg[0], dg[1]), pk(dg[2], dg[3]));
+                            *reinterpret_cast<uint2*>(sg + S_COLS) = make_uint2(pk(du[0], du[1]), pk(du[2], du[3]));
                         }
                         if (dp_part) {
                             // lanes l and l + 32 hold the two halves of the row's 32 columns
@@ -1045,8 +1057,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                         const int r = i * 32 + (lane & 31);
                         const int u = j * 8 + q * 2 + (lane >> 5);
                         uint2 v;
-                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
-                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                        v.x = pk(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                        v.y = pk(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
                         *reinterpret_cast<uint2*>(stg + r * 64 + ((u ^ ((r >> 1) & 15)) << 2)) = v;
                     }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1157,8 +1169,8 @@ void grouped_gemm_kernel(const GemmParams p) {
                             const uint2 hu = *reinterpret_cast<const uint2*>(sU + off);
                             const uint32_t gw[2] = {hg.x, hg.y};
                             const uint32_t uw[2] = {hu.x, hu.y};
-                            const uint32_t dw[2] = {pack2(acc_rd(acc[i][j][q * 4]), acc_rd(acc[i][j][q * 4 + 1])),
-                                                    pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]))};
+                            const uint32_t dw[2] = {pk(acc_rd(acc[i][j][q * 4]), acc_rd(acc[i][j][q * 4 + 1])),
+                                                    pk(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]))};
                             float dg[4], du[4];
 #pragma unroll
                             for (int x = 0; x < 4; ++x) {
@@ -1172,9 +1184,9 @@ void grouped_gemm_kernel(const GemmParams p) {
                                 if (cv) dps += da * (g * sgm * u);
                             }
                             *reinterpret_cast<uint2*>(sG + off) =
-                                make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+                                make_uint2(pk(dg[0], dg[1]), pk(dg[2], dg[3]));
                             *reinterpret_cast<uint2*>(sU + off) =
-                                make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
+                                make_uint2(pk(du[0], du[1]), pk(du[2], du[3]));
                         }
                         if (dp_part) {
                             // same per-lane order and halves as the streaming flavor

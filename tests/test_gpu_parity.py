@@ -119,18 +119,22 @@ def test_tiny_workload():
     # the maximum expert count: mostly 0..5 rows, one large expert in the middle
     ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 64, 64),
     # four-wave forward tiles (H % 256 == 0, F % 128 == 0): full and partial
-    # tiles, streamed tails on both sides of 96 rows, one- and two-iteration K loops
+    # tiles, streamed tails on both sides of 96 rows, one- and two-iteration K
+    # loops; its few thin items fit the grid twice over, so each runs as two
+    # column halves
     ([17, 0, 255, 256, 257, 600, 97, 96], 256, 128),
     ([300, 1, 0, 2, 130, 513], 512, 256),
     ([0, 700, 129, 0, 256], 256, 512),
     ([130, 0, 513, 40], 256, 1024),   # FC2 on four-wave tiles from F = 1024
     # 279 small experts and 17 of 512 rows: taking the small ones as partial
     # tiles would add a round, so they stay streaming items beside the tiles
+    # (four-wave: 279 thin items, more than half the grid, run whole)
     ([512 if i % 18 == 0 else 40 for i in range(296)], 256, 128),
     # the maximum expert count with fragment copies: the four-wave tiles find
     # their expert among 1024 beside the streaming launch
     ([300 if i == 500 else (i * 7919) % 6 for i in range(1024)], 256, 128),
-    # only thin items in the four-wave kernel: small experts at a shape with fragment copies
+    # only thin items in the four-wave kernel: small experts at a shape with
+    # fragment copies (40 thin items on a grid of 92: column halves)
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33, 96, 1], 512, 256),
     # many small experts, as in the small-batch workload
     ([24, 0, 19, 31, 27, 22, 0, 25, 30, 18, 26, 21, 0, 29, 23, 17, 28, 24, 20, 33,
