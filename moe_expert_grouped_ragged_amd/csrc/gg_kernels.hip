@@ -165,6 +165,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(uni_ptr(base)), "s"(uni(lds)) : "memory", "m0");
 }
+// The same copy marked non-temporal (low retention in the caches), for data
+// read once per pass: the streamed weights of the streaming items, which
+// would otherwise push out of L2 the token panels that every item re-reads.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(uni_ptr(base)), "s"(uni(lds)) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Read one accumulator register in the epilogue.  The accumulators live in
@@ -648,7 +655,7 @@ void grouped_gemm_kernel(const GemmParams p) {
                     const int cc = (s_sh && c >= S_CPR / 2) ? c - S_CPR / 2 : c;
                     voff = static_cast<uint32_t>((min(k0 + kr, K - 1) * p.ldw + min(it.col0 + cc * 8, N - 8)) * 2);
                 }
-                dma16(wb, voff, base + (cw * SW_PW + i) * 1024);
+                dma16_nt(wb, voff, base + (cw * SW_PW + i) * 1024);
             }
             const uint16_t* xb = p.act + static_cast<int64_t>(it.row0) * K;
 #pragma unroll
