@@ -8,12 +8,13 @@
 // with no rows own no tiles, so their weights are never read.
 //
 // Two kernels.  The eight-wave kernel (grouped_gemm_kernel) runs every GEMM
-// over the row-major packed weights, and always the dgrad FC2; the four-wave
-// kernel (tile4_kernel, below) runs FC1, FC2 and dX when the caller also
-// passes a fragment-ordered copy of the weights.  In the eight-wave kernel two flavors share one launch.  Rows
-// that fill 256-row tiles run as 256 x 256
-// output tiles; the at most 96 rows an expert leaves over (all rows of a
-// small expert) run as weight-streaming items, before the tiles.  An item is
+// over the row-major packed weights; the four-wave kernel (tile4_kernel,
+// below) runs FC1, FC2, dX and, for plain SwiGLU, the dgrad FC2 when the
+// caller also passes a fragment-ordered copy of the weights.  In the
+// eight-wave kernel two flavors share one launch.  Rows that fill 256-row
+// tiles run as 256 x 256 output tiles; the at most 96 rows an expert leaves
+// over (all rows of a small expert) run as weight-streaming items, before the
+// tiles.  An item is
 // those rows x 192 weight rows (six compute waves of 32 rows; two more waves
 // issue every copy into a 4-stage ring), or x 96 weight rows when the items
 // fit into the grid twice over, so that they spread over all workgroups.
