@@ -1641,19 +1641,24 @@ void tile4_kernel(const GemmParams p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-        // prologue: virtual steps -13..-1 (weights of steps -6..6, token stages
-        // 0..2 and the first copy of stage 3); step -1 ends like the last step
-        // of a stage: stage 0 is in, and its first step's fragments are read
+        // prologue: virtual steps -13..-1 (weights of steps 0..6 from step -7
+        // on, token stages 0..2 and the first copy of stage 3); step -1 ends
+        // like the last step of a stage: stage 0 is in, and its first step's
+        // fragments are read.  Steps -13..-8 issue no weight loads: they come
+        // before the first one, so no weight wait counts them, and 28 loads
+        // follow stage 0's last copy (steps -9 and -8 issue two, -7..-2 four).
 #pragma unroll
         for (int g = -13; g < 0; ++g) {
             const int gw = g + 7;
             if (g == -1) {
-                wait_vmcnt<32>();    // this wave's copies of stage 0
+                wait_vmcnt<28>();    // this wave's copies of stage 0
                 block_barrier();
                 rd_t(0, 0);
             }
+            if (gw >= 0) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) wfrag_load(wr[(gw + 8) & 7][j], wptr(gw < 0 ? 0 : gw, j));
+                for (int j = 0; j < 2; ++j) wfrag_load(wr[gw & 7][j], wptr(gw, j));
+            }
             tdma(((g + 1) >> 2) + 3, (g + 1) & 3);
         }
         for (int g0 = 0; g0 < nsteps; g0 += 8) {
