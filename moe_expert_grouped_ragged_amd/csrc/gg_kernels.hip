@@ -1434,13 +1434,20 @@ void tile4_kernel(const GemmParams p) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        // prologue: virtual steps -12..-1; steps -12..-8 issue no weight loads
+        // (they come before the first one, so no weight wait counts them).
+        // Stage 0's last copy is then followed by 22 loads, not the 24 the
+        // loop's stage wait assumes, so the prologue waits for it here.
 #pragma unroll
         for (int g = -12; g < 0; ++g) {
             const int gw = g + 7;
+            if (gw >= 0) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) wfrag_load_m(wr[(gw + 8) & 7][j], wp(gw < 0 ? 0 : gw, j), j ? lm1 : lm0);
+                for (int j = 0; j < 2; ++j) wfrag_load_m(wr[gw & 7][j], wp(gw, j), j ? lm1 : lm0);
+            }
             tdma1((g >> 2) + 3, g & 3);
         }
+        wait_vmcnt<22>();
         for (int g0 = 0; g0 < nsteps; g0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
