@@ -1255,8 +1255,10 @@ void grouped_gemm_kernel(const GemmParams p) {
 // are complete at vmcnt(26) and a thin item's at vmcnt(19); a thin item's
 // stage copies are complete at vmcnt(24), and in tiles the weight wait of a
 // stage's last step already covers the next stage's copies.  Virtual steps
-// before step 0 repeat the pattern as the prologue, and the steps past the
-// end re-load clamped addresses, so the counts hold everywhere.  The sums are
+// before step 0 repeat the pattern as the prologue (without the weight loads
+// that would come before the first real one, which no wait counts), and the
+// steps past the end re-load clamped addresses, so the counts hold
+// everywhere.  The sums are
 // the same MFMA chain over k as in the eight-wave tiles and the streaming
 // items, so a row's results do not depend on which flavor computed it.
 //
