@@ -1844,6 +1844,13 @@ void tile4_kernel(const GemmParams p) {
                 // the buffer's reads are done before a copy refills it
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             };
+            // The compiler skips a store instruction whose 64 lanes all lie
+            // past the tile, so the counts that include stores hold only
+            // where all of them are issued: pass 0 always (a tile has more
+            // than 96 rows), passes 1 and 2 in full tiles.  A partial tile
+            // waits for every store before the copy it needs instead, so no
+            // copy of it is still in flight when the next tile's copies land.
+            const bool full = rows == TBM;
             h1_copy(0, 0);
             h1_copy(1, 1);
             wait_vmcnt<16>();                       // pass 0 has landed
@@ -1854,10 +1861,12 @@ void tile4_kernel(const GemmParams p) {
             h1_compute(GrpTag<1>{}, 1);
             h1_store(1, 1);
             h1_copy(3, 1);
-            wait_vmcnt<32>();                       // pass 2
+            if (full) wait_vmcnt<32>();             // pass 2 (then the stores of pass 1, the copy of pass 3)
+            else wait_vmcnt<16>();
             h1_compute(GrpTag<2>{}, 0);
             h1_store(2, 0);
-            wait_vmcnt<16>();                       // pass 3
+            if (full) wait_vmcnt<16>();             // pass 3 (then the stores of pass 2)
+            else wait_vmcnt<0>();
             h1_compute(GrpTag<3>{}, 1);
             h1_store(3, 1);
         }
