@@ -1393,484 +1393,498 @@ void tile4_kernel(const GemmParams p) {
     constexpr bool THIN_HALVES = EPI != EPI_DSWIGLU;
     const int h_sh = (THIN_HALVES && 2 * n_items <= G) ? 1 : 0;   // log2 of the work units per thin item
     const int n_units = n_items << h_sh;
-    int wi = slot;
-    for (; wi < n_units; wi += G) {
-        const int ti = wi >> h_sh;     // thin item
-        const int hf = wi & h_sh;      // its half (0 for a whole item)
-        const int e = uni(find_expert(s_spre, E, ti));
-        const int local = ti - uni(s_spre[e]);
-        const int rb = uni(s_off[e]);
-        const int re = uni(s_off[e + 1]);
-        const int row0 = uni(rb + tile_rows_of(re - rb));
-        const int rows = re - row0;                          // 1 .. 96
-        const int col0 = uni(local * TILE_COLS);
-        const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
-        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
-        const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (h_sh ? hf : (wave >> 1))) * 4 + (wave & 1)
-                                            : col0 / 32 + (h_sh ? 4 * hf + wave : 2 * wave);
-        const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : (h_sh ? tb0 : tb0 + 1);
-        // loads whose results a half item does not store move one lane only
-        const bool rep0 = h_sh && EPI == EPI_SWIGLU && wave >= 2;
-        const bool rep1 = h_sh && (EPI != EPI_SWIGLU || wave >= 2);
-        const uint64_t lm0 = uni(rep0) ? 1ull : ~0ull;
-        const uint64_t lm1 = uni(rep1) ? 1ull : ~0ull;
-        auto wp = [&](int g, int j) -> const uint16_t* {
-            return wfe + ((static_cast<int64_t>(j ? tb1 : tb0) * nsteps + g) * 64 + lane) * 8;
-        };
-        auto tdma1 = [&](int s, int part) {
-            const int ss = s < kiters ? s : kiters - 1;
-            const int r = min((tid >> 3) + 32 * part, rows - 1);
-            const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * part) * 16;
-            dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
-        };
-        auto rd3 = [&](int g, int buf) {
-            const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
-            const int ch = 2 * (g & 3) + (lane >> 5);
+    // Workgroup s takes units s, s + G, ... of the work list (thin units,
+    // then tiles).  The workgroups of every other XCD (blockIdx mod 8) run
+    // their tiles before their thin units, so that half of the chip reaches
+    // the tile boundaries (the epilogue stores and the next tile's first
+    // loads) at other times than the other half, while the workgroups of one
+    // XCD, which share operand panels in its L2, stay in step.
+    const bool tiles_first = (b & 1) != 0;
+    int t_first = slot;
+    if (t_first < n_units) t_first += (n_units - t_first + G - 1) / G * G;
+    t_first -= n_units;
+    for (int phase = 0; phase < 2; ++phase) {
+        const bool thin_now = (phase == 0) != tiles_first;
+        for (int wi = thin_now ? slot : n_units; wi < n_units; wi += G) {
+            const int ti = wi >> h_sh;     // thin item
+            const int hf = wi & h_sh;      // its half (0 for a whole item)
+            const int e = uni(find_expert(s_spre, E, ti));
+            const int local = ti - uni(s_spre[e]);
+            const int rb = uni(s_off[e]);
+            const int re = uni(s_off[e + 1]);
+            const int row0 = uni(rb + tile_rows_of(re - rb));
+            const int rows = re - row0;                          // 1 .. 96
+            const int col0 = uni(local * TILE_COLS);
+            const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
+            const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
+            const int tb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (h_sh ? hf : (wave >> 1))) * 4 + (wave & 1)
+                                                : col0 / 32 + (h_sh ? 4 * hf + wave : 2 * wave);
+            const int tb1 = (EPI == EPI_SWIGLU) ? tb0 + 2 : (h_sh ? tb0 : tb0 + 1);
+            // loads whose results a half item does not store move one lane only
+            const bool rep0 = h_sh && EPI == EPI_SWIGLU && wave >= 2;
+            const bool rep1 = h_sh && (EPI != EPI_SWIGLU || wave >= 2);
+            const uint64_t lm0 = uni(rep0) ? 1ull : ~0ull;
+            const uint64_t lm1 = uni(rep1) ? 1ull : ~0ull;
+            auto wp = [&](int g, int j) -> const uint16_t* {
+                return wfe + ((static_cast<int64_t>(j ? tb1 : tb0) * nsteps + g) * 64 + lane) * 8;
+            };
+            auto tdma1 = [&](int s, int part) {
+                const int ss = s < kiters ? s : kiters - 1;
+                const int r = min((tid >> 3) + 32 * part, rows - 1);
+                const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * part) * 16;
+                dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
+            };
+            auto rd3 = [&](int g, int buf) {
+                const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
+                const int ch = 2 * (g & 3) + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
+            };
 #pragma unroll
             for (int i = 0; i < 3; ++i)
-                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
-        };
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            // prologue: virtual steps -12..-1; steps -12..-8 issue no weight loads
+            // (they come before the first one, so no weight wait counts them).
+            // Stage 0's last copy is then followed by 22 loads, not the 24 the
+            // loop's stage wait assumes, so the prologue waits for it here.
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-        // prologue: virtual steps -12..-1; steps -12..-8 issue no weight loads
-        // (they come before the first one, so no weight wait counts them).
-        // Stage 0's last copy is then followed by 22 loads, not the 24 the
-        // loop's stage wait assumes, so the prologue waits for it here.
+            for (int g = -12; g < 0; ++g) {
+                const int gw = g + 7;
+                if (gw >= 0) {
 #pragma unroll
-        for (int g = -12; g < 0; ++g) {
-            const int gw = g + 7;
-            if (gw >= 0) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) wfrag_load_m(wr[gw & 7][j], wp(gw, j), j ? lm1 : lm0);
-            }
-            tdma1((g >> 2) + 3, g & 3);
-        }
-        wait_vmcnt<22>();
-        for (int g0 = 0; g0 < nsteps; g0 += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int g = g0 + u;
-                const int j4 = u & 3;
-                if (j4 == 0) {
-                    wait_vmcnt<24>();
-                    block_barrier();
-                    rd3(g, u & 1);
+                    for (int j = 0; j < 2; ++j) wfrag_load_m(wr[gw & 7][j], wp(gw, j), j ? lm1 : lm0);
                 }
-                if (j4 < 3) rd3(g + 1, (u + 1) & 1);
-                wfrag_wait19(wr[u][0], wr[u][1]);
+                tdma1((g >> 2) + 3, g & 3);
+            }
+            wait_vmcnt<22>();
+            for (int g0 = 0; g0 < nsteps; g0 += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int g = g0 + u;
+                    const int j4 = u & 3;
+                    if (j4 == 0) {
+                        wait_vmcnt<24>();
+                        block_barrier();
+                        rd3(g, u & 1);
+                    }
+                    if (j4 < 3) rd3(g + 1, (u + 1) & 1);
+                    wfrag_wait19(wr[u][0], wr[u][1]);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
+                    const int gw = g + 7;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        wfrag_load_m(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j), j ? lm1 : lm0);
+                    tdma1((g >> 2) + 3, j4);
+                }
+            }
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
+            block_barrier();
+            mfma_drain();
+            int opaque = 0;
+            asm volatile("" : "+s"(opaque));
+            const int trow0 = row0 + opaque;
+            uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
+            if constexpr (EPI == EPI_STORE) {
+                // [96 rows][64 cols] bf16; 16-byte chunk c of row r at c ^ (r & 7)
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
-                const int gw = g + 7;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    wfrag_load_m(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j), j ? lm1 : lm0);
-                tdma1((g >> 2) + 3, j4);
-            }
-        }
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
-        block_barrier();
-        mfma_drain();
-        int opaque = 0;
-        asm volatile("" : "+s"(opaque));
-        const int trow0 = row0 + opaque;
-        uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
-        if constexpr (EPI == EPI_STORE) {
-            // [96 rows][64 cols] bf16; 16-byte chunk c of row r at c ^ (r & 7)
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = i * 32 + (lane & 31);
-                        const int c = j * 4 + q;
-                        uint2 v;
-                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
-                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
-                        *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5)) = v;
-                    }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // a half item's wave stores its first 32 columns (block tb0) only
-            const int gcol0 = col0 + (h_sh ? 128 * hf + 32 * wave : 64 * wave);
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = i * 32 + (lane & 31);
+                            const int c = j * 4 + q;
+                            uint2 v;
+                            v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                            v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                            *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (lane >> 5)) = v;
+                        }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                // a half item's wave stores its first 32 columns (block tb0) only
+                const int gcol0 = col0 + (h_sh ? 128 * hf + 32 * wave : 64 * wave);
 #pragma unroll 4
-            for (int sidx = 0; sidx < 12; ++sidx) {
-                const int idx = sidx * 64 + lane;
-                const int r = idx >> 3, c = idx & 7;
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (r & 7)) << 3));
-                const int oc = p.h1_order ? h1_col(tb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
-                if (r < rows && (!h_sh || c < 4))
-                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
-            }
-        } else if constexpr (EPI == EPI_DSWIGLU) {
-            // The saved gate and up values of the wave's 64 features for the
-            // item's rows, [96 rows][gate 64 | up 64] bf16 (256-byte rows,
-            // 24 KiB), are copied into the staging area with LDS-DMA (rows past
-            // the item repeat its last row); 16-byte chunk c (0..7 gate, 8..15
-            // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The results
-            // overwrite them in place and leave as whole row segments of dH1.
-            const int F = N;
-            const int f0 = col0 + 64 * wave + opaque;
-            const int ln = lane + opaque;     // per-lane values computed here, not above the K loop
-            const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
-            const uint32_t sl = lds_addr(stg);
-#pragma unroll
-            for (int d = 0; d < 24; ++d) {
-                const int r = 4 * d + (ln >> 4), pc = ln & 15;
-                const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
-                const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
-                dma16(hb, static_cast<uint32_t>((min(r, rows - 1) * 2 * F + col) * 2), sl + d * 1024);
-            }
-            wait_vmcnt<0>();
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int r = i * 32 + (ln & 31);
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int pos = (4 * j + q) ^ (r & 7);
-                        uint16_t* pg = stg + r * 128 + pos * 8 + 4 * (ln >> 5);
-                        dswiglu_inplace(pg, pg + 64, acc[i][j], q);
-                    }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll 4
-            for (int d = 0; d < 24; ++d) {
-                const int r = 4 * d + (ln >> 4), pc = ln & 15;
-                const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 8);
-                const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
-                if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * (2 * F) + col) = v;
-            }
-        } else {
-            // [96 rows][32 features] bf16 arrays for A, gate and up; 16-byte
-            // chunk c of row r at c ^ (r & 3)
-            uint16_t* sA = stg;
-            uint16_t* sG = stg + 3072;
-            uint16_t* sU = stg + 6144;
-            // a half item's features are stored by waves 0 and 1
-            const int fcol0 = col0 + (h_sh ? 64 * hf : 0) + 32 * wave;
-            const bool owns = !h_sh || wave < 2;
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int r = i * 32 + (lane & 31);
-                const float pr = (probs && r < rows) ? probs[trow0 + r] : 1.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (lane >> 5);
-                    swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr, *reinterpret_cast<uint2*>(sA + off),
-                            *reinterpret_cast<uint2*>(sG + off), *reinterpret_cast<uint2*>(sU + off));
+                for (int sidx = 0; sidx < 12; ++sidx) {
+                    const int idx = sidx * 64 + lane;
+                    const int r = idx >> 3, c = idx & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + ((c ^ (r & 7)) << 3));
+                    const int oc = p.h1_order ? h1_col(tb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
+                    if (r < rows && (!h_sh || c < 4))
+                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
                 }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll 2
-            for (int sidx = 0; sidx < 6; ++sidx) {
-                const int idx = sidx * 64 + lane;
-                const int r = idx >> 2, c = idx & 3;
-                const int off = r * 32 + ((c ^ (r & 3)) << 3);
-                const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
-                const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
-                const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
-                if (r < rows && owns) {
-                    *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + fcol0 + c * 8) = va;
-                    if (p.out1) {
-                        uint16_t* h = p.out1 + static_cast<int64_t>(trow0 + r) * (2 * N) + fcol0 + c * 8;
-                        *reinterpret_cast<uint4*>(h) = vg;
-                        *reinterpret_cast<uint4*>(h + N) = vu;
-                    }
+            } else if constexpr (EPI == EPI_DSWIGLU) {
+                // The saved gate and up values of the wave's 64 features for the
+                // item's rows, [96 rows][gate 64 | up 64] bf16 (256-byte rows,
+                // 24 KiB), are copied into the staging area with LDS-DMA (rows past
+                // the item repeat its last row); 16-byte chunk c (0..7 gate, 8..15
+                // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The results
+                // overwrite them in place and leave as whole row segments of dH1.
+                const int F = N;
+                const int f0 = col0 + 64 * wave + opaque;
+                const int ln = lane + opaque;     // per-lane values computed here, not above the K loop
+                const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
+                const uint32_t sl = lds_addr(stg);
+#pragma unroll
+                for (int d = 0; d < 24; ++d) {
+                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                    dma16(hb, static_cast<uint32_t>((min(r, rows - 1) * 2 * F + col) * 2), sl + d * 1024);
                 }
-            }
-        }
-        block_barrier();   // staging reads done before the next copies land
-    }
-
-    // ---- then the 256-row tiles.  Wave w owns all 256 token rows and its own
-    // 64 weight rows (two 32-row blocks: for SwiGLU the gate and up rows of 32
-    // features, else 64 output columns), as 8 x 2 accumulator blocks of
-    // 32 x 32 (all 256 AGPRs).  So no two waves load the same weight bytes:
-    // per k16 step a workgroup moves 8 KiB of weights and 8 KiB of token
-    // copies through the vector-memory path, and each wave reads the step's
-    // eight token fragments from the LDS ring, one step ahead.  Per k16 step
-    // every wave issues two weight loads (seven steps ahead) and two of the
-    // eight token copies of a stage three stages ahead: stage s + 4 in steps
-    // 4s + 3 .. 4s + 6, after the barrier of step 4s + 3 (the last of stage s)
-    // has freed slot s % 4.  A step's weights are complete at vmcnt(26)
-    // (2 + 6 x 4), and that wait in step 4s + 3 also covers this wave's
-    // copies of stage s + 1, the last of which has 28 loads after it; so the
-    // barrier there lets every wave read the first fragments of stage s + 1
-    // a step ahead like all others.
-    for (int t = wi - n_units; t < n_tiles; t += G) {
-        const int e = uni(find_expert(s_pre, E, t));
-        const int local = t - uni(s_pre[e]);
-        const int rb = uni(s_off[e]);
-        const int row_end = uni(s_off[e + 1]);
-        const int tiles_m = tiles_m_of(row_end - rb);
-        const int row0 = uni(rb + (local % tiles_m) * TBM);
-        const int col0 = uni((local / tiles_m) * TILE_COLS);
-        const int rows = min(TBM, row_end - row0);
-        const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
-        const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
-        // this wave's two 32-row blocks in fragment order (W1's blocks go gate,
-        // gate, up, up per 64 features)
-        const int wb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
-        const int wb1 = (EPI == EPI_SWIGLU) ? wb0 + 2 : wb0 + 1;
-        auto wptr = [&](int g, int j) -> const uint16_t* {
-            return wfe + ((static_cast<int64_t>(j ? wb1 : wb0) * nsteps + g) * 64 + lane) * 8;
-        };
-        // two of the eight LDS-DMA instructions of token stage s (clamped to the last)
-        auto tdma = [&](int s, int part) {
-            const int ss = s < kiters ? s : kiters - 1;
+                wait_vmcnt<0>();
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = 2 * part + u;
-                const int r = min((tid >> 3) + 32 * i, rows - 1);
-                const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * i) * 16;
-                dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
-            }
-        };
-        auto rd_t = [&](int g, int buf) {   // the eight token fragments of step g
-            const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
-            const int ch = 2 * (g & 3) + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
-        };
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-        // prologue: virtual steps -13..-1 (weights of steps 0..6 from step -7
-        // on, token stages 0..2 and the first copy of stage 3); step -1 ends
-        // like the last step of a stage: stage 0 is in, and its first step's
-        // fragments are read.  Steps -13..-8 issue no weight loads: they come
-        // before the first one, so no weight wait counts them, and 28 loads
-        // follow stage 0's last copy (steps -9 and -8 issue two, -7..-2 four).
-#pragma unroll
-        for (int g = -13; g < 0; ++g) {
-            const int gw = g + 7;
-            if (g == -1) {
-                wait_vmcnt<28>();    // this wave's copies of stage 0
-                block_barrier();
-                rd_t(0, 0);
-            }
-            if (gw >= 0) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) wfrag_load(wr[gw & 7][j], wptr(gw, j));
-            }
-            tdma(((g + 1) >> 2) + 3, (g + 1) & 3);
-        }
-        for (int g0 = 0; g0 < nsteps; g0 += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int g = g0 + u;
-                const int j4 = u & 3;
-                // this step's weights; in a stage's last step also this wave's
-                // copies of the next stage (28 loads were issued after them)
-                wfrag_wait26(wr[u][0], wr[u][1]);
-                // In a stage's last step: every wave's copies of the next
-                // stage are in, and every wave has read all of this stage's
-                // fragments, so its slot may be refilled from here on.
-                if (j4 == 3) block_barrier();
-                rd_t(g + 1, (u + 1) & 1);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < 3; ++i) {
+                    const int r = i * 32 + (ln & 31);
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
-                const int gw = g + 7;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
-                tdma(((g + 1) >> 2) + 3, (j4 + 1) & 3);
-                // issue order within the step: one token fragment read for the
-                // next step after each of the first eight MFMAs, so the reads
-                // spread over the step instead of bunching behind its MFMAs
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        for (int q = 0; q < 4; ++q) {
+                            const int pos = (4 * j + q) ^ (r & 7);
+                            uint16_t* pg = stg + r * 128 + pos * 8 + 4 * (ln >> 5);
+                            dswiglu_inplace(pg, pg + 64, acc[i][j], q);
+                        }
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            }
-        }
-        // drain the clamped loads; the ring becomes the epilogue's staging area
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
-        block_barrier();
-        mfma_drain();
-        // Values derived below are computed here, not hoisted above the K loop.
-        int opaque = 0;
-        asm volatile("" : "+s"(opaque));
-        const int trow0 = row0 + opaque;
-        const int ln = lane + opaque;
-        uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
-        // Lane holds token row (ln & 31) of each token block i and, for
-        // register 4q + x of block j, weight row 32j + 8q + 4(ln >> 5) + x of
-        // the wave's 64.
-        if constexpr (EPI == EPI_STORE) {
-            // [256 rows][64 cols] bf16 (128-byte rows); 16-byte chunk c of row r at c ^ (r & 7)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = i * 32 + (ln & 31);
-                        const int c = j * 4 + q;
-                        uint2 v;
-                        v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
-                        v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
-                        *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (ln >> 5)) = v;
-                    }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const int gcol0 = col0 + 64 * wave;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 4
-            for (int sidx = 0; sidx < 32; ++sidx) {
-                const int idx = sidx * 64 + ln;
-                const int r = idx >> 3, pc = idx & 7;
-                const int c = pc ^ (r & 7);
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + pc * 8);
-                const int oc = p.h1_order ? h1_col(wb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
-                if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
-            }
-        } else if constexpr (EPI == EPI_SWIGLU) {
-            // two passes of 128 token rows; per pass [128][32] bf16 arrays for
-            // A, gate and up (64-byte rows); 16-byte chunk c of row r at c ^ (r & 3)
-            uint16_t* sA = stg;
-            uint16_t* sG = stg + 4096;
-            uint16_t* sU = stg + 8192;
-            const int fcol0 = col0 + 32 * wave;        // first feature of this wave
+                for (int d = 0; d < 24; ++d) {
+                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 8);
+                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                    if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * (2 * F) + col) = v;
+                }
+            } else {
+                // [96 rows][32 features] bf16 arrays for A, gate and up; 16-byte
+                // chunk c of row r at c ^ (r & 3)
+                uint16_t* sA = stg;
+                uint16_t* sG = stg + 3072;
+                uint16_t* sU = stg + 6144;
+                // a half item's features are stored by waves 0 and 1
+                const int fcol0 = col0 + (h_sh ? 64 * hf : 0) + 32 * wave;
+                const bool owns = !h_sh || wave < 2;
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int i = pass * 4 + ii;
-                    const int r = ii * 32 + (ln & 31);
-                    const int prow = trow0 + pass * 128 + r;
-                    const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
+                for (int i = 0; i < 3; ++i) {
+                    const int r = i * 32 + (lane & 31);
+                    const float pr = (probs && r < rows) ? probs[trow0 + r] : 1.0f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (ln >> 5);
+                        const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (lane >> 5);
                         swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr, *reinterpret_cast<uint2*>(sA + off),
                                 *reinterpret_cast<uint2*>(sG + off), *reinterpret_cast<uint2*>(sU + off));
                     }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 2
-                for (int sidx = 0; sidx < 8; ++sidx) {
-                    const int idx = sidx * 64 + ln;
-                    const int r = idx >> 2, pc = idx & 3;
-                    const int c = pc ^ (r & 3);
-                    const int off = r * 32 + pc * 8;
-                    const int grow = trow0 + pass * 128 + r;
+                for (int sidx = 0; sidx < 6; ++sidx) {
+                    const int idx = sidx * 64 + lane;
+                    const int r = idx >> 2, c = idx & 3;
+                    const int off = r * 32 + ((c ^ (r & 3)) << 3);
                     const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
                     const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
                     const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
-                    if (grow < row_end) {
-                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + fcol0 + c * 8) = va;
+                    if (r < rows && owns) {
+                        *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + fcol0 + c * 8) = va;
                         if (p.out1) {
-                            uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + fcol0 + c * 8;
+                            uint16_t* h = p.out1 + static_cast<int64_t>(trow0 + r) * (2 * N) + fcol0 + c * 8;
                             *reinterpret_cast<uint4*>(h) = vg;
                             *reinterpret_cast<uint4*>(h + N) = vu;
                         }
                     }
                 }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
-        } else {
-            // SwiGLU derivative.  Per pass of 64 token rows (token blocks 2p,
-            // 2p + 1) the saved gate and up values of the wave's 64 features,
-            // [64 rows][gate 64 | up 64] bf16 (256-byte rows, 16 KiB), are
-            // copied into one of two staging buffers with LDS-DMA (rows past
-            // the tile repeat its last row); 16-byte chunk c (0..7 gate, 8..15
-            // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The next
-            // pass's copy is in flight while a pass is computed in place and
-            // stored as whole row segments of dH1.  The waits count this wave's
-            // memory operations in issue order: 16 copies or 16 stores a pass.
-            const int F = N;
-            const int f0 = col0 + 64 * wave + opaque;
-            const int trows = rows + opaque;
-            const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
-            const uint32_t sl = lds_addr(stg);
-            auto h1_copy = [&](int pass, int buf) {
+            block_barrier();   // staging reads done before the next copies land
+        }
+
+        // ---- then the 256-row tiles.  Wave w owns all 256 token rows and its own
+        // 64 weight rows (two 32-row blocks: for SwiGLU the gate and up rows of 32
+        // features, else 64 output columns), as 8 x 2 accumulator blocks of
+        // 32 x 32 (all 256 AGPRs).  So no two waves load the same weight bytes:
+        // per k16 step a workgroup moves 8 KiB of weights and 8 KiB of token
+        // copies through the vector-memory path, and each wave reads the step's
+        // eight token fragments from the LDS ring, one step ahead.  Per k16 step
+        // every wave issues two weight loads (seven steps ahead) and two of the
+        // eight token copies of a stage three stages ahead: stage s + 4 in steps
+        // 4s + 3 .. 4s + 6, after the barrier of step 4s + 3 (the last of stage s)
+        // has freed slot s % 4.  A step's weights are complete at vmcnt(26)
+        // (2 + 6 x 4), and that wait in step 4s + 3 also covers this wave's
+        // copies of stage s + 1, the last of which has 28 loads after it; so the
+        // barrier there lets every wave read the first fragments of stage s + 1
+        // a step ahead like all others.
+        for (int t = thin_now ? n_tiles : t_first; t < n_tiles; t += G) {
+            const int e = uni(find_expert(s_pre, E, t));
+            const int local = t - uni(s_pre[e]);
+            const int rb = uni(s_off[e]);
+            const int row_end = uni(s_off[e + 1]);
+            const int tiles_m = tiles_m_of(row_end - rb);
+            const int row0 = uni(rb + (local % tiles_m) * TBM);
+            const int col0 = uni((local / tiles_m) * TILE_COLS);
+            const int rows = min(TBM, row_end - row0);
+            const uint16_t* a_base = p.act + static_cast<int64_t>(row0) * K;
+            const uint16_t* wfe = p.wfrag + static_cast<int64_t>(e) * p.wfrag_stride;
+            // this wave's two 32-row blocks in fragment order (W1's blocks go gate,
+            // gate, up, up per 64 features)
+            const int wb0 = (EPI == EPI_SWIGLU) ? (col0 / 64 + (wave >> 1)) * 4 + (wave & 1) : col0 / 32 + 2 * wave;
+            const int wb1 = (EPI == EPI_SWIGLU) ? wb0 + 2 : wb0 + 1;
+            auto wptr = [&](int g, int j) -> const uint16_t* {
+                return wfe + ((static_cast<int64_t>(j ? wb1 : wb0) * nsteps + g) * 64 + lane) * 8;
+            };
+            // two of the eight LDS-DMA instructions of token stage s (clamped to the last)
+            auto tdma = [&](int s, int part) {
+                const int ss = s < kiters ? s : kiters - 1;
 #pragma unroll
-                for (int d = 0; d < 16; ++d) {
-                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
-                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
-                    const int trow = min(pass * 64 + r, trows - 1);
-                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
-                    dma16(hb, static_cast<uint32_t>((trow * 2 * F + col) * 2), sl + buf * 16384 + d * 1024);
+                for (int u = 0; u < 2; ++u) {
+                    const int i = 2 * part + u;
+                    const int r = min((tid >> 3) + 32 * i, rows - 1);
+                    const uint32_t lds = ring_l + (s & 3) * (T4_SLOT * 2) + (wave * 64 + T4_THREADS * i) * 16;
+                    dma16(a_base, static_cast<uint32_t>((r * K + ss * BK + lc) * 2), lds);
                 }
             };
-            auto h1_compute = [&](auto pass_tag, int buf) {
-                constexpr int pass = decltype(pass_tag)::value;
-                uint16_t* bb = stg + buf * 8192;
+            auto rd_t = [&](int g, int buf) {   // the eight token fragments of step g
+                const uint16_t* st = s_ring + ((g >> 2) & 3) * T4_SLOT;
+                const int ch = 2 * (g & 3) + (lane >> 5);
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int r = ii * 32 + (ln & 31);
+                for (int i = 0; i < 8; ++i)
+                    tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
+            };
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            // prologue: virtual steps -13..-1 (weights of steps 0..6 from step -7
+            // on, token stages 0..2 and the first copy of stage 3); step -1 ends
+            // like the last step of a stage: stage 0 is in, and its first step's
+            // fragments are read.  Steps -13..-8 issue no weight loads: they come
+            // before the first one, so no weight wait counts them, and 28 loads
+            // follow stage 0's last copy (steps -9 and -8 issue two, -7..-2 four).
+#pragma unroll
+            for (int g = -13; g < 0; ++g) {
+                const int gw = g + 7;
+                if (g == -1) {
+                    wait_vmcnt<28>();    // this wave's copies of stage 0
+                    block_barrier();
+                    rd_t(0, 0);
+                }
+                if (gw >= 0) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) wfrag_load(wr[gw & 7][j], wptr(gw, j));
+                }
+                tdma(((g + 1) >> 2) + 3, (g + 1) & 3);
+            }
+            for (int g0 = 0; g0 < nsteps; g0 += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int g = g0 + u;
+                    const int j4 = u & 3;
+                    // this step's weights; in a stage's last step also this wave's
+                    // copies of the next stage (28 loads were issued after them)
+                    wfrag_wait26(wr[u][0], wr[u][1]);
+                    // In a stage's last step: every wave's copies of the next
+                    // stage are in, and every wave has read all of this stage's
+                    // fragments, so its slot may be refilled from here on.
+                    if (j4 == 3) block_barrier();
+                    rd_t(g + 1, (u + 1) & 1);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
+                    const int gw = g + 7;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
+                    tdma(((g + 1) >> 2) + 3, (j4 + 1) & 3);
+                    // issue order within the step: one token fragment read for the
+                    // next step after each of the first eight MFMAs, so the reads
+                    // spread over the step instead of bunching behind its MFMAs
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                }
+            }
+            // drain the clamped loads; the ring becomes the epilogue's staging area
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
+            block_barrier();
+            mfma_drain();
+            // Values derived below are computed here, not hoisted above the K loop.
+            int opaque = 0;
+            asm volatile("" : "+s"(opaque));
+            const int trow0 = row0 + opaque;
+            const int ln = lane + opaque;
+            uint16_t* stg = s_ring + wave * T4_SLOT + opaque;   // 32 KiB per wave
+            // Lane holds token row (ln & 31) of each token block i and, for
+            // register 4q + x of block j, weight row 32j + 8q + 4(ln >> 5) + x of
+            // the wave's 64.
+            if constexpr (EPI == EPI_STORE) {
+                // [256 rows][64 cols] bf16 (128-byte rows); 16-byte chunk c of row r at c ^ (r & 7)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const int pos = (4 * j + q) ^ (r & 7);
-                            uint16_t* pg = bb + r * 128 + pos * 8 + 4 * (ln >> 5);
-                            dswiglu_inplace(pg, pg + 64, acc[2 * pass + ii][j], q);
+                            const int r = i * 32 + (ln & 31);
+                            const int c = j * 4 + q;
+                            uint2 v;
+                            v.x = pack2(acc_rd(acc[i][j][q * 4 + 0]), acc_rd(acc[i][j][q * 4 + 1]));
+                            v.y = pack2(acc_rd(acc[i][j][q * 4 + 2]), acc_rd(acc[i][j][q * 4 + 3]));
+                            *reinterpret_cast<uint2*>(stg + r * 64 + ((c ^ (r & 7)) << 3) + 4 * (ln >> 5)) = v;
                         }
-                }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            };
-            auto h1_store = [&](int pass, int buf) {
-                const uint16_t* bb = stg + buf * 8192;
+                const int gcol0 = col0 + 64 * wave;
+#pragma unroll 4
+                for (int sidx = 0; sidx < 32; ++sidx) {
+                    const int idx = sidx * 64 + ln;
+                    const int r = idx >> 3, pc = idx & 7;
+                    const int c = pc ^ (r & 7);
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + pc * 8);
+                    const int oc = p.h1_order ? h1_col(wb0 + (c >> 2), F_of(N)) + (c & 3) * 8 : gcol0 + c * 8;
+                    if (r < rows) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(trow0 + r) * N + oc) = v;
+                }
+            } else if constexpr (EPI == EPI_SWIGLU) {
+                // two passes of 128 token rows; per pass [128][32] bf16 arrays for
+                // A, gate and up (64-byte rows); 16-byte chunk c of row r at c ^ (r & 3)
+                uint16_t* sA = stg;
+                uint16_t* sG = stg + 4096;
+                uint16_t* sU = stg + 8192;
+                const int fcol0 = col0 + 32 * wave;        // first feature of this wave
 #pragma unroll
-                for (int d = 0; d < 16; ++d) {
-                    const int r = 4 * d + (ln >> 4), pc = ln & 15;
-                    const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
-                    const uint4 v = *reinterpret_cast<const uint4*>(bb + r * 128 + pc * 8);
-                    const int grow = trow0 + pass * 64 + r;
-                    const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
-                    if (grow < row_end) *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * (2 * F) + col) = v;
+                for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int i = pass * 4 + ii;
+                        const int r = ii * 32 + (ln & 31);
+                        const int prow = trow0 + pass * 128 + r;
+                        const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int off = r * 32 + ((q ^ (r & 3)) << 3) + 4 * (ln >> 5);
+                            swiglu4(acc[i][0], acc[i][1], q, slope, pr, probs != nullptr,
+                                    *reinterpret_cast<uint2*>(sA + off), *reinterpret_cast<uint2*>(sG + off),
+                                    *reinterpret_cast<uint2*>(sU + off));
+                        }
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+                    for (int sidx = 0; sidx < 8; ++sidx) {
+                        const int idx = sidx * 64 + ln;
+                        const int r = idx >> 2, pc = idx & 3;
+                        const int c = pc ^ (r & 3);
+                        const int off = r * 32 + pc * 8;
+                        const int grow = trow0 + pass * 128 + r;
+                        const uint4 va = *reinterpret_cast<const uint4*>(sA + off);
+                        const uint4 vg = *reinterpret_cast<const uint4*>(sG + off);
+                        const uint4 vu = *reinterpret_cast<const uint4*>(sU + off);
+                        if (grow < row_end) {
+                            *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * N + fcol0 + c * 8) = va;
+                            if (p.out1) {
+                                uint16_t* h = p.out1 + static_cast<int64_t>(grow) * (2 * N) + fcol0 + c * 8;
+                                *reinterpret_cast<uint4*>(h) = vg;
+                                *reinterpret_cast<uint4*>(h + N) = vu;
+                            }
+                        }
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 }
-                // the buffer's reads are done before a copy refills it
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            };
-            // The compiler skips a store instruction whose 64 lanes all lie
-            // past the tile, so the counts that include stores hold only
-            // where all of them are issued: pass 0 always (a tile has more
-            // than 96 rows), passes 1 and 2 in full tiles.  A partial tile
-            // waits for every store before the copy it needs instead, so no
-            // copy of it is still in flight when the next tile's copies land.
-            const bool full = rows == TBM;
-            h1_copy(0, 0);
-            h1_copy(1, 1);
-            wait_vmcnt<16>();                       // pass 0 has landed
-            h1_compute(GrpTag<0>{}, 0);
-            h1_store(0, 0);
-            h1_copy(2, 0);
-            wait_vmcnt<32>();                       // pass 1 (then the stores of pass 0, the copy of pass 2)
-            h1_compute(GrpTag<1>{}, 1);
-            h1_store(1, 1);
-            h1_copy(3, 1);
-            if (full) wait_vmcnt<32>();             // pass 2 (then the stores of pass 1, the copy of pass 3)
-            else wait_vmcnt<16>();
-            h1_compute(GrpTag<2>{}, 0);
-            h1_store(2, 0);
-            if (full) wait_vmcnt<16>();             // pass 3 (then the stores of pass 2)
-            else wait_vmcnt<0>();
-            h1_compute(GrpTag<3>{}, 1);
-            h1_store(3, 1);
+            } else {
+                // SwiGLU derivative.  Per pass of 64 token rows (token blocks 2p,
+                // 2p + 1) the saved gate and up values of the wave's 64 features,
+                // [64 rows][gate 64 | up 64] bf16 (256-byte rows, 16 KiB), are
+                // copied into one of two staging buffers with LDS-DMA (rows past
+                // the tile repeat its last row); 16-byte chunk c (0..7 gate, 8..15
+                // up) of row r sits at (c & 8) | ((c & 7) ^ (r & 7)).  The next
+                // pass's copy is in flight while a pass is computed in place and
+                // stored as whole row segments of dH1.  The waits count this wave's
+                // memory operations in issue order: 16 copies or 16 stores a pass.
+                const int F = N;
+                const int f0 = col0 + 64 * wave + opaque;
+                const int trows = rows + opaque;
+                const uint16_t* hb = p.aux + static_cast<int64_t>(row0) * (2 * F);
+                const uint32_t sl = lds_addr(stg);
+                auto h1_copy = [&](int pass, int buf) {
+#pragma unroll
+                    for (int d = 0; d < 16; ++d) {
+                        const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                        const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                        const int trow = min(pass * 64 + r, trows - 1);
+                        const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                        dma16(hb, static_cast<uint32_t>((trow * 2 * F + col) * 2), sl + buf * 16384 + d * 1024);
+                    }
+                };
+                auto h1_compute = [&](auto pass_tag, int buf) {
+                    constexpr int pass = decltype(pass_tag)::value;
+                    uint16_t* bb = stg + buf * 8192;
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int r = ii * 32 + (ln & 31);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int pos = (4 * j + q) ^ (r & 7);
+                                uint16_t* pg = bb + r * 128 + pos * 8 + 4 * (ln >> 5);
+                                dswiglu_inplace(pg, pg + 64, acc[2 * pass + ii][j], q);
+                            }
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                };
+                auto h1_store = [&](int pass, int buf) {
+                    const uint16_t* bb = stg + buf * 8192;
+#pragma unroll
+                    for (int d = 0; d < 16; ++d) {
+                        const int r = 4 * d + (ln >> 4), pc = ln & 15;
+                        const int c = (pc & 8) | ((pc & 7) ^ (r & 7));
+                        const uint4 v = *reinterpret_cast<const uint4*>(bb + r * 128 + pc * 8);
+                        const int grow = trow0 + pass * 64 + r;
+                        const int col = (c < 8 ? 0 : F) + f0 + 8 * (c & 7);
+                        if (grow < row_end)
+                            *reinterpret_cast<uint4*>(p.out0 + static_cast<int64_t>(grow) * (2 * F) + col) = v;
+                    }
+                    // the buffer's reads are done before a copy refills it
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                };
+                // The compiler skips a store instruction whose 64 lanes all lie
+                // past the tile, so the counts that include stores hold only
+                // where all of them are issued: pass 0 always (a tile has more
+                // than 96 rows), passes 1 and 2 in full tiles.  A partial tile
+                // waits for every store before the copy it needs instead, so no
+                // copy of it is still in flight when the next tile's copies land.
+                const bool full = rows == TBM;
+                h1_copy(0, 0);
+                h1_copy(1, 1);
+                wait_vmcnt<16>();                       // pass 0 has landed
+                h1_compute(GrpTag<0>{}, 0);
+                h1_store(0, 0);
+                h1_copy(2, 0);
+                wait_vmcnt<32>();                       // pass 1 (then the stores of pass 0, the copy of pass 2)
+                h1_compute(GrpTag<1>{}, 1);
+                h1_store(1, 1);
+                h1_copy(3, 1);
+                if (full) wait_vmcnt<32>();             // pass 2 (then the stores of pass 1, the copy of pass 3)
+                else wait_vmcnt<16>();
+                h1_compute(GrpTag<2>{}, 0);
+                h1_store(2, 0);
+                if (full) wait_vmcnt<16>();             // pass 3 (then the stores of pass 2)
+                else wait_vmcnt<0>();
+                h1_compute(GrpTag<3>{}, 1);
+                h1_store(3, 1);
+            }
+            block_barrier();   // staging reads done before the next tile's copies land
         }
-        block_barrier();   // staging reads done before the next tile's copies land
     }
 }
 
