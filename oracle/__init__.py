@@ -64,10 +64,16 @@ def _load():
                 getattr(lib, name).argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, p, p]
             for name in ("oracle_dgrad_glu_f32", "oracle_dgrad_glu_f64"):
                 getattr(lib, name).argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, p, p, p]
+            for name in ("oracle_scale_rows_f32", "oracle_scale_rows_f64"):
+                getattr(lib, name).argtypes = [i64, i64, p, p, p]
+            for name in ("oracle_scale_rows_bwd_f32", "oracle_scale_rows_bwd_f64"):
+                getattr(lib, name).argtypes = [i64, i64, p, p, p, p, p]
             for name in ("oracle_round_bf16", "oracle_forward_f32", "oracle_forward_f64",
                          "oracle_dgrad_f32", "oracle_dgrad_f64", "oracle_swiglu_f32", "oracle_fc2_f32",
                          "oracle_dgrad_fc1_f32", "oracle_glu_f32", "oracle_forward_glu_f32",
-                         "oracle_forward_glu_f64", "oracle_dgrad_glu_f32", "oracle_dgrad_glu_f64"):
+                         "oracle_forward_glu_f64", "oracle_dgrad_glu_f32", "oracle_dgrad_glu_f64",
+                         "oracle_scale_rows_f32", "oracle_scale_rows_f64", "oracle_scale_rows_bwd_f32",
+                         "oracle_scale_rows_bwd_f64"):
                 getattr(lib, name).restype = None
             _lib = lib
     return _lib
@@ -331,6 +337,51 @@ def dgrad_glu64(dy, h1, offsets, w1, w2, act="swiglu", probs=None):
     _load().oracle_dgrad_glu_f64(E, H, F, _ptr(off), _act(act), _optr(pr), _ptr(dy), _ptr(h1), _ptr(w1),
                                  _ptr(w2), _ptr(dh1), _ptr(dx), _ptr(dp))
     return {"dh1": dh1, "dx": dx, "dprobs": dp}
+
+
+def scale_rows(x, probs):
+    """Router probability on the FC1 input: x [M,H] -> bf16(p_r * x_r) [M,H]
+    (fp32 product rounded once), every row."""
+    x32 = _as_f32(x)
+    M, H = x32.shape
+    pr = _probs(probs, M)
+    out = np.full((M, H), np.nan, np.float32)
+    _load().oracle_scale_rows_f32(M, H, _ptr(pr), _ptr(x32), _ptr(out))
+    return out
+
+
+def scale_rows_backward(g, x, probs):
+    """Input gradient of scale_rows given g = dL/dx' [M,H] and the unscaled
+    x [M,H]: dx = bf16(p_r * g_r), dprobs [M] = sum_h g*x (fp32)."""
+    g32, x32 = _as_f32(g), _as_f32(x)
+    M, H = x32.shape
+    assert g32.shape == (M, H)
+    pr = _probs(probs, M)
+    dx = np.full((M, H), np.nan, np.float32)
+    dp = np.full(M, np.nan, np.float32)
+    _load().oracle_scale_rows_bwd_f32(M, H, _ptr(pr), _ptr(g32), _ptr(x32), _ptr(dx), _ptr(dp))
+    return {"dx": dx, "dprobs": dp}
+
+
+def scale_rows64(x, probs):
+    """fp64 scale_rows without rounding."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    M, H = x.shape
+    pr = _probs(probs, M, np.float64)
+    out = np.full((M, H), np.nan)
+    _load().oracle_scale_rows_f64(M, H, _ptr(pr), _ptr(x), _ptr(out))
+    return out
+
+
+def scale_rows_backward64(g, x, probs):
+    """fp64 scale_rows_backward without rounding."""
+    g, x = (np.ascontiguousarray(v, dtype=np.float64) for v in (g, x))
+    M, H = x.shape
+    pr = _probs(probs, M, np.float64)
+    dx = np.full((M, H), np.nan)
+    dp = np.full(M, np.nan)
+    _load().oracle_scale_rows_bwd_f64(M, H, _ptr(pr), _ptr(g), _ptr(x), _ptr(dx), _ptr(dp))
+    return {"dx": dx, "dprobs": dp}
 
 
 def sample_rows(offsets, rows):

@@ -33,6 +33,18 @@
 // with act'(g) = s (1 + c g (1 - s)), s = sigmoid(c g).  dp is an fp32 sum
 // over j in increasing order and is not rounded to bf16.
 //
+// Router probability on the FC1 input (paged-stash pull request, "What does
+// this PR do": the optional multiply by the probability before FC1, the
+// other of the two places a router probability enters).  No formula is
+// printed; the reading used here scales the routed row before FC1, after
+// which the expert MLP runs with the plain activation:
+//     x'_r  = p_r x_r
+// and, given g = dL/dx' (the input gradient of the MLP at x'),
+//     dx_r  = p_r g_r
+//     dp_r  = sum_h g[r, h] x[r, h]        (increasing h, not rounded)
+// In the float instantiation x' and dx are the fp32 products rounded once
+// to bf16, as every other stage.
+//
 // Precision.  Two instantiations of the same code:
 //   float  : inputs are bf16 values held in fp32, every sum accumulates in
 //            fp32 in increasing index order, and H1, A, Y, dA, dH1, dX are
@@ -249,6 +261,28 @@ void dgrad_fc1_all(int64_t E, int64_t H, int64_t F, const int64_t* off, const T*
     }
 }
 
+// x'_r = p_r x_r for every row r < M (x, out [M][H], probs [M]).
+template <typename T>
+void scale_rows_all(int64_t M, int64_t H, const T* probs, const T* x, T* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; ++r)
+        for (int64_t h = 0; h < H; ++h) out[r * H + h] = rnd<T>(probs[r] * x[r * H + h]);
+}
+
+// Its input gradient: dx_r = p_r g_r and dp_r = sum_h g[r, h] x[r, h].
+template <typename T>
+void scale_rows_bwd_all(int64_t M, int64_t H, const T* probs, const T* g, const T* x, T* dx, T* dprobs) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; ++r) {
+        T s = 0;
+        for (int64_t h = 0; h < H; ++h) {
+            dx[r * H + h] = rnd<T>(probs[r] * g[r * H + h]);
+            s += g[r * H + h] * x[r * H + h];
+        }
+        if (dprobs) dprobs[r] = s;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -340,6 +374,27 @@ void oracle_dgrad_glu_f64(int64_t E, int64_t H, int64_t F, const int64_t* offset
                           const double* probs, const double* dy, const double* h1, const double* w1,
                           const double* w2, double* dh1, double* dx, double* dprobs) {
     dgrad_all<double>(E, H, F, offsets, act, probs, dy, h1, w1, w2, dh1, dx, dprobs);
+}
+
+// Router probability on the FC1 input: x [M][H] -> out [M][H].
+void oracle_scale_rows_f32(int64_t M, int64_t H, const float* probs, const float* x, float* out) {
+    scale_rows_all<float>(M, H, probs, x, out);
+}
+
+// Its input gradient: g [M][H] (gradient at the scaled input), x [M][H]
+// (the unscaled input) -> dx [M][H], dprobs [M] (may be null).
+void oracle_scale_rows_bwd_f32(int64_t M, int64_t H, const float* probs, const float* g, const float* x,
+                               float* dx, float* dprobs) {
+    scale_rows_bwd_all<float>(M, H, probs, g, x, dx, dprobs);
+}
+
+void oracle_scale_rows_f64(int64_t M, int64_t H, const double* probs, const double* x, double* out) {
+    scale_rows_all<double>(M, H, probs, x, out);
+}
+
+void oracle_scale_rows_bwd_f64(int64_t M, int64_t H, const double* probs, const double* g, const double* x,
+                               double* dx, double* dprobs) {
+    scale_rows_bwd_all<double>(M, H, probs, g, x, dx, dprobs);
 }
 
 }  // extern "C"
