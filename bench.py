@@ -18,7 +18,7 @@ GPU: 128 experts, 32768 tokens x top-8 (each expert's rows padded up to a
 multiple of 256), hidden 4096, FFN 2048.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--layout auto|frag|packed]
-                    [--activation swiglu|qgeglu] [--weighted] [--recompute]
+                    [--activation swiglu|qgeglu] [--weighted | --probs-on-input] [--recompute]
 
 Weights: the packed buffer alone (6*E*H*F bytes, the library's default) and,
 for shapes with H % 256 == 0 and F % 128 == 0, also with the opt-in
@@ -30,8 +30,11 @@ the copies' arm (the faster), and "layouts" gives both.
 --activation / --weighted time the QuickGeGLU and router-probability-weighted
 variants (gg_forward_fc1_glu + gg_forward_fc2 + gg_dgrad_glu, dprobs
 included); --recompute keeps no H1 and recomputes FC1 inside the dgrad call
-(gg_dgrad_recompute; the step's counted work stays 12*M*H*F).  The default
-line is plain SwiGLU with a saved H1.
+(gg_dgrad_recompute; the step's counted work stays 12*M*H*F).
+--probs-on-input scales the FC1 input rows by the router probabilities
+instead (gg_scale_rows before FC1 and gg_scale_rows_backward after the
+input gradient, both timed in the step; their HBM rooflines are in
+roofline.row_scaling).  The default line is plain SwiGLU with a saved H1.
 """
 from __future__ import annotations
 
@@ -88,9 +91,11 @@ def load_traffic(workload_name: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
+def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None, probs_in=None):
     """The CPU oracle, as it stands, on the first k rows of every non-empty
-    expert (k calibrated to about target_s seconds of work)."""
+    expert (k calibrated to about target_s seconds of work).  probs weights
+    the activation; probs_in instead scales the FC1 input rows (the scale and
+    its gradient then run around the plain path)."""
     import numpy as np
     import torch
 
@@ -112,7 +117,12 @@ def cpu_baseline(case, target_s: float, act: str = "swiglu", probs=None):
         xs = case.x[torch.from_numpy(rows)]
         dys = case.dy[torch.from_numpy(rows)]
         t0 = time.perf_counter()
-        if act == "swiglu" and probs is None:
+        if probs_in is not None:
+            pin = probs_in[rows]
+            fw = oracle.forward(oracle.scale_rows(xs, pin), comp, w1, w2)
+            dg = oracle.dgrad(dys, fw["h1"], comp, w1, w2)
+            dg = {"dx": oracle.scale_rows_backward(dg["dx"], xs, pin)["dx"]}
+        elif act == "swiglu" and probs is None:
             fw = oracle.forward(xs, comp, w1, w2)
             dg = oracle.dgrad(dys, fw["h1"], comp, w1, w2)
         else:
@@ -286,6 +296,10 @@ def main():
     ap.add_argument("--weighted", action="store_true",
                     help="weight the activation by a per-row router probability (fp32, seeded "
                          "uniform in [0.05, 1)) and return its gradient dprobs from the dgrad")
+    ap.add_argument("--probs-on-input", action="store_true",
+                    help="router probabilities scale the FC1 input rows (gg_scale_rows before FC1, "
+                         "gg_scale_rows_backward after the input gradient, both in the step) instead of "
+                         "weighting the activation")
     ap.add_argument("--recompute", action="store_true",
                     help="forward without saving H1 and input gradient through gg_dgrad_recompute "
                          "(FC1 recomputed from X inside the dgrad call)")
@@ -346,17 +360,35 @@ def main():
     y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     dx = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    if args.weighted and args.probs_on_input:
+        print("bench.py: --weighted and --probs-on-input are alternatives", file=sys.stderr)
+        sys.exit(2)
     glu = args.activation != "swiglu" or args.weighted or args.recompute
+    with_probs = args.weighted or args.probs_on_input
     probs_np = (np.random.default_rng(w.seed + 17).uniform(0.05, 1.0, M).astype(np.float32)
-                if args.weighted else None)
-    probs = torch.from_numpy(probs_np).to(dev) if args.weighted else None
-    dprobs = torch.empty(M, dtype=torch.float32, device=dev) if args.weighted else None
+                if with_probs else None)
+    probs_all = torch.from_numpy(probs_np).to(dev) if with_probs else None
+    probs = probs_all if args.weighted else None          # at the activation
+    dprobs = torch.empty(M, dtype=torch.float32, device=dev) if with_probs else None
+    # probabilities on the input: the scaled rows and the gradient at them
+    xs = torch.empty(M, H, dtype=torch.bfloat16, device=dev) if args.probs_on_input else None
+    dxs = torch.empty(M, H, dtype=torch.bfloat16, device=dev) if args.probs_on_input else None
+    x_in = xs if args.probs_on_input else x
+    dx_mlp = dxs if args.probs_on_input else dx
     ws_glu = torch.empty(gg.dgrad_glu_workspace_bytes(M, F, args.weighted), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(arm, ev):
         fr = frag if arm == "frag" else None
+        if args.probs_on_input:
+            if ev is not None:
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+            gg.gg_scale_rows(x, probs_all, out=xs)
+            if ev is not None:
+                s1.record(stream)
+                ev["scale_rows"].append((s0, s1))
         if ev is not None:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -364,11 +396,12 @@ def main():
             e3 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         if args.recompute:
-            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, save_h1=False, a_out=a, frag=fr)
+            gg.gg_forward_fc1_glu(x_in, off, packed, E, H, F, args.activation, probs, save_h1=False, a_out=a,
+                                  frag=fr)
         elif glu or fr is not None:
-            gg.gg_forward_fc1_glu(x, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a, frag=fr)
+            gg.gg_forward_fc1_glu(x_in, off, packed, E, H, F, args.activation, probs, h1_out=h1, a_out=a, frag=fr)
         else:
-            gg.gg_forward_fc1_swiglu(x, off, packed, E, H, F, h1_out=h1, a_out=a)
+            gg.gg_forward_fc1_swiglu(x_in, off, packed, E, H, F, h1_out=h1, a_out=a)
         if ev is not None:
             e1.record(stream)
         if fr is None:
@@ -378,18 +411,28 @@ def main():
         if ev is not None:
             e2.record(stream)
         if args.recompute:
-            gg.gg_dgrad_recompute(dy, x, off, packed, E, H, F, args.activation, probs,
-                                  want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs, frag=fr)
+            gg.gg_dgrad_recompute(dy, x_in, off, packed, E, H, F, args.activation, probs,
+                                  want_dprobs=args.weighted, workspace=ws_glu, dx=dx_mlp,
+                                  dprobs=dprobs if args.weighted else None, frag=fr)
         elif glu or fr is not None:
             gg.gg_dgrad_glu(dy, h1, off, packed, E, H, F, args.activation, probs,
-                            want_dprobs=args.weighted, workspace=ws_glu, dx=dx, dprobs=dprobs, frag=fr)
+                            want_dprobs=args.weighted, workspace=ws_glu, dx=dx_mlp,
+                            dprobs=dprobs if args.weighted else None, frag=fr)
         else:
-            gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx)
+            gg.gg_dgrad(dy, h1, off, packed, E, H, F, workspace=ws, dx=dx_mlp)
         if ev is not None:
             e3.record(stream)
             ev["fc1"].append((e0, e1))
             ev["fc2"].append((e1, e2))
             ev["dgrad"].append((e2, e3))
+        if args.probs_on_input:
+            if ev is not None:
+                b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b0.record(stream)
+            gg.gg_scale_rows_backward(dxs, x, probs_all, dx=dx, dprobs=dprobs)
+            if ev is not None:
+                b1.record(stream)
+                ev["scale_rows_bwd"].append((b0, b1))
 
     if args.launch_ab:
         print(json.dumps(launch_ab(gg, case, x, dy, off, packed, h1, a, y, ws, dx, stream, args)), flush=True)
@@ -408,7 +451,8 @@ def main():
         torch.sum(flush_rd, dim=0, dtype=torch.int64, out=sink)
 
     def timed_arm(arm):
-        ev = {k: [] for k in ("fc1", "fc2", "dgrad")}
+        ev = {k: [] for k in ("fc1", "fc2", "dgrad") + (("scale_rows", "scale_rows_bwd") if args.probs_on_input
+                                                         else ())}
         for i in range(args.warmup):
             evict(i)
             step(arm, None)
@@ -420,7 +464,7 @@ def main():
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps          # includes the evictions
         per_step = {k: np.array([s.elapsed_time(e) for s, e in v]) for k, v in ev.items()}
-        steps_ms = per_step["fc1"] + per_step["fc2"] + per_step["dgrad"]
+        steps_ms = sum(per_step.values())
         return {"ms_per_step": float(np.median(steps_ms)), "ms_per_step_min": float(np.min(steps_ms)),
                 "wall_ms_per_step_incl_eviction": wall_ms,
                 "per_call_ms": {k: float(np.median(v)) for k, v in per_step.items()},
@@ -460,6 +504,16 @@ def main():
     roof.update({"traffic": None if glu else load_traffic(args.workload, f"fc1_{arms[0]}"),
                  "median_launch_ms": fc1_ms, "min_launch_ms": call_min_ms["fc1"],
                  "flops_per_launch": fc1_flops, "algorithmic_bytes_per_launch": fc1_bytes})
+    if args.probs_on_input:
+        # the two row-scaling kernels are bound by HBM: the scale reads x and
+        # probs and writes x' (4MH + 4M bytes); its gradient reads dx' and x
+        # and probs and writes dx and dprobs (6MH + 8M bytes)
+        rows_bytes = {"scale_rows": 4.0 * M * H + 4.0 * M, "scale_rows_bwd": 6.0 * M * H + 8.0 * M}
+        roof["row_scaling"] = {
+            k: {"bound": "hbm", "algorithmic_bytes_per_launch": b, "median_launch_ms": call_ms[k],
+                "achieved": b / (call_ms[k] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": b / (call_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            for k, b in rows_bytes.items()}
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -468,7 +522,8 @@ def main():
                    "routed_rows": M, "real_rows": int(case.counts.sum()), "hidden": H, "ffn": F,
                    "routing": w.routing, "pad_to": w.pad_to,
                    "parallelism": "single-gpu", "activation": args.activation,
-                   "weighted": bool(args.weighted), "recompute_fc1_in_dgrad": bool(args.recompute),
+                   "weighted": bool(args.weighted), "probs_on_input": bool(args.probs_on_input),
+                   "recompute_fc1_in_dgrad": bool(args.recompute),
                    "weights": ("packed buffer (6*E*H*F bytes) + opt-in fragment-ordered copies (12*E*H*F bytes)"
                                if arms[0] == "frag" else "packed buffer (6*E*H*F bytes)")},
         "timing": "median over the timed steps of HIP-event step times on the launch stream; a 1 GiB "
@@ -488,7 +543,9 @@ def main():
         "device": device_record(dev, clocks),
     }
     if not args.no_cpu_baseline:
-        rec, sample = cpu_baseline(case, args.cpu_seconds, args.activation, probs_np)
+        rec, sample = cpu_baseline(case, args.cpu_seconds, args.activation,
+                                   probs_np if args.weighted else None,
+                                   probs_np if args.probs_on_input else None)
         out["cpu_baseline"] = rec
         out["parity"] = parity_of_sample(sample, y, dx)
     else:

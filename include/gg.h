@@ -220,6 +220,30 @@ int gg_dgrad_recompute(const void* dy, const void* x, const int64_t* offsets, in
                        void* workspace, size_t workspace_bytes, void* dx, float* dprobs,
                        hipStream_t stream);
 
+/* ---- Router probability on the FC1 input.  The paged-stash pull request
+ * ("[Main] Support paged stash with device-initiated GroupedLinear", "What
+ * does this PR do") names two places where a routed row's probability can
+ * enter the expert MLP: the activation boundary (gg_forward_fc1_glu's probs)
+ * and an optional multiply before FC1, which the fused path does not run.
+ * These two calls are that multiply and its input gradient, for use around
+ * the plain calls (gg_forward_fc1_swiglu ... gg_dgrad on the scaled rows).
+ * The pages give no formula; this library reads them as
+ *   x'[r][h]  = bf16(p_r * x[r][h])            (fp32 product, nearest even)
+ *   dx[r][h]  = bf16(p_r * dxs[r][h])          (dxs = dL/dx', e.g. gg_dgrad's dx)
+ *   dprobs[r] = sum_h dxs[r][h] * x[r][h]      (fp32, not rounded)
+ * for every row r < M (not only the routed ones; there are no offsets).
+ * x, x_out, dxs, dx: DEVICE bf16 [M][H], 16-byte aligned; probs, dprobs:
+ * DEVICE fp32 [M], 4-byte aligned.  H % 8 == 0, else GG_ERR_INVALID_ARGUMENT.
+ * x_out may be x, and dx may be dxs (in place); any other overlap of an
+ * output with an input or another output gives GG_ERR_ALIASING.  dprobs may
+ * be NULL.  The sum of dprobs[r] has one fixed order (one wavefront per row:
+ * lane l adds 16-byte chunks l, l + 64, ... in increasing h, then the lane
+ * sums are combined pairwise, lanes 32 apart first).  One launch on
+ * `stream` each; M == 0 returns GG_OK without one. */
+int gg_scale_rows(const void* x, const float* probs, int64_t M, int64_t H, void* x_out, hipStream_t stream);
+int gg_scale_rows_backward(const void* dxs, const void* x, const float* probs, int64_t M, int64_t H,
+                           void* dx, float* dprobs, hipStream_t stream);
+
 /* ---- For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).
  * gg_dgrad without a workspace argument: dH1 goes to a static device array

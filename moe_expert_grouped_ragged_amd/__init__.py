@@ -20,7 +20,12 @@ current stream.  The functions carry the C names:
 
 The *_glu calls add the QuickGeGLU activation and the weighting of the
 activation by each row's router probability (fp32 [M]), with dp of that
-weight from the input gradient.
+weight from the input gradient.  The probability can instead scale the FC1
+input rows:
+
+  gg_scale_rows(x, probs)                        -> x' = bf16(p_r * x_r)
+  gg_scale_rows_backward(dxs, x, probs)          -> (dx, dprobs)
+        (ScaleRows is the autograd form, to compose with FrozenExpertMLP)
 
 Frozen, bias-free bf16 expert weights only: the Megatron-LM pull request
 "perf(moe): add frozen grouped GEMM for adapter training" (section "Why
@@ -86,9 +91,11 @@ def _load() -> ctypes.CDLL:
     lib.gg_forward_fc1_glu.argtypes = [p, p, i64, p, p, i64, i64, i64, i32, p, p, p, p]
     lib.gg_dgrad_glu.argtypes = [p, p, p, i64, p, p, i64, i64, i64, i32, p, p, sz, p, p, p]
     lib.gg_dgrad_recompute.argtypes = [p, p, p, i64, p, p, i64, i64, i64, i32, p, p, sz, p, p, p]
+    lib.gg_scale_rows.argtypes = [p, p, i64, i64, p, p]
+    lib.gg_scale_rows_backward.argtypes = [p, p, p, i64, i64, p, p, p]
     for name in ("gg_pack_weights", "gg_pack_frag", "gg_forward_fc1_swiglu", "gg_forward_fc2",
                  "gg_forward_fc2_frag", "gg_dgrad", "gg_round_bf16", "gg_forward_fc1_glu", "gg_dgrad_glu",
-                 "gg_dgrad_recompute", "gg_dgrad_noalloc"):
+                 "gg_dgrad_recompute", "gg_dgrad_noalloc", "gg_scale_rows", "gg_scale_rows_backward"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -483,6 +490,63 @@ def gg_round_bf16(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -
     _check(lib.gg_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream_ptr(stream)),
            "gg_round_bf16")
     return out
+
+
+def gg_scale_rows(x: torch.Tensor, probs: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Router probability on the FC1 input: out [M, H] = bf16(probs[r] * x[r])
+    for every row (out may be x).  x bf16 [M, H]; probs fp32 [M]."""
+    x = _bf16_cuda(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, H]")
+    M, H = x.shape
+    pr = _probs_cuda(probs, M, x.device)
+    if pr is None:
+        raise ValueError("probs is required")
+    out = _out(out, (M, H), "out", x.device)
+    _check(lib.gg_scale_rows(x.data_ptr(), pr.data_ptr(), M, H, out.data_ptr(), _stream_ptr(stream)),
+           "gg_scale_rows")
+    return out
+
+
+def gg_scale_rows_backward(dxs: torch.Tensor, x: torch.Tensor, probs: torch.Tensor, want_dprobs: bool = True,
+                           dx: Optional[torch.Tensor] = None, dprobs: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None):
+    """Input gradient of gg_scale_rows given dxs = dL/dx' [M, H] and the
+    unscaled x: (dx = bf16(probs[r] * dxs[r]), dprobs[r] = sum_h dxs*x in fp32
+    or None).  dx may be dxs."""
+    dxs = _bf16_cuda(dxs, "dxs")
+    if dxs.dim() != 2:
+        raise ValueError("dxs must be [M, H]")
+    M, H = dxs.shape
+    x = _bf16_cuda(x, "x", (M, H), dxs.device)
+    pr = _probs_cuda(probs, M, dxs.device)
+    if pr is None:
+        raise ValueError("probs is required")
+    dx = _out(dx, (M, H), "dx", dxs.device)
+    dprobs = _probs_cuda(dprobs, M, dxs.device, "dprobs")
+    if dprobs is None and want_dprobs:
+        dprobs = torch.empty(M, dtype=torch.float32, device=dxs.device)
+    _check(lib.gg_scale_rows_backward(dxs.data_ptr(), x.data_ptr(), pr.data_ptr(), M, H, dx.data_ptr(),
+                                      _ptr(dprobs), _stream_ptr(stream)), "gg_scale_rows_backward")
+    return dx, dprobs
+
+
+class ScaleRows(torch.autograd.Function):
+    """Autograd wrapper of gg_scale_rows: x' = bf16(probs[r] * x[r]); the
+    backward gives dx and, when probs requires grad, dprobs."""
+
+    @staticmethod
+    def forward(ctx, x, probs):
+        ctx.save_for_backward(x, probs)
+        return gg_scale_rows(x, probs.detach())
+
+    @staticmethod
+    def backward(ctx, g):
+        x, probs = ctx.saved_tensors
+        dx, dprobs = gg_scale_rows_backward(g.contiguous(), x, probs.detach(),
+                                            want_dprobs=ctx.needs_input_grad[1])
+        return dx, dprobs
 
 
 class FrozenExpertMLP(torch.autograd.Function):

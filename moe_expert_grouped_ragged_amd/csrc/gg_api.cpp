@@ -459,6 +459,49 @@ int gg_dgrad_noalloc(const void* dy, const void* h1, const int64_t* offsets, int
                       static_cast<size_t>(GG_NOALLOC_SCRATCH_BYTES), dx, nullptr, stream);
 }
 
+int gg_scale_rows(const void* x, const float* probs, int64_t M, int64_t H, void* x_out, hipStream_t stream) {
+    if (M < 0 || M >= (int64_t(1) << 31) || H <= 0 || H % 8 != 0 || H >= (int64_t(1) << 22))
+        return GG_ERR_INVALID_ARGUMENT;
+    if (M == 0) return GG_OK;
+    if (!x || !probs || !x_out) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(x_out) || !aligned4(probs)) return GG_ERR_MISALIGNED;
+    const size_t xb = static_cast<size_t>(M * H) * 2;
+    const Range out = range_of(x_out, xb);
+    if ((x != x_out && overlap(out, range_of(x, xb))) || overlap(out, range_of(probs, M * 4)))
+        return GG_ERR_ALIASING;
+    DeviceInfo info;
+    const int st = device_info(stream, &info);
+    if (st != GG_OK) return st;
+    return gg::launch_scale_rows(static_cast<const uint16_t*>(x), probs, M, static_cast<int>(H),
+                                 static_cast<uint16_t*>(x_out), stream) == hipSuccess
+               ? GG_OK
+               : GG_ERR_HIP;
+}
+
+int gg_scale_rows_backward(const void* dxs, const void* x, const float* probs, int64_t M, int64_t H, void* dx,
+                           float* dprobs, hipStream_t stream) {
+    if (M < 0 || M >= (int64_t(1) << 31) || H <= 0 || H % 8 != 0 || H >= (int64_t(1) << 22))
+        return GG_ERR_INVALID_ARGUMENT;
+    if (M == 0) return GG_OK;
+    if (!dxs || !x || !probs || !dx) return GG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dxs) || !aligned16(x) || !aligned16(dx) || !aligned4(probs) || (dprobs && !aligned4(dprobs)))
+        return GG_ERR_MISALIGNED;
+    const size_t xb = static_cast<size_t>(M * H) * 2;
+    const Range rdx = range_of(dx, xb), rx = range_of(x, xb), rp = range_of(probs, M * 4);
+    const Range rdp = dprobs ? range_of(dprobs, M * 4) : Range{0, 0};
+    // dx may be dxs itself; nothing else may overlap an output
+    if ((dx != dxs && overlap(rdx, range_of(dxs, xb))) || overlap(rdx, rx) || overlap(rdx, rp) ||
+        overlap(rdp, range_of(dxs, xb)) || overlap(rdp, rx) || overlap(rdp, rp) || overlap(rdp, rdx))
+        return GG_ERR_ALIASING;
+    DeviceInfo info;
+    const int st = device_info(stream, &info);
+    if (st != GG_OK) return st;
+    return gg::launch_scale_rows_bwd(static_cast<const uint16_t*>(dxs), static_cast<const uint16_t*>(x), probs, M,
+                                     static_cast<int>(H), static_cast<uint16_t*>(dx), dprobs, stream) == hipSuccess
+               ? GG_OK
+               : GG_ERR_HIP;
+}
+
 int gg_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
     if (n < 0) return GG_ERR_INVALID_ARGUMENT;
     if (n == 0) return GG_OK;

@@ -54,6 +54,13 @@ static_assert(FRAG_W2 - FRAG_W1 == 2 && FRAG_W1T - FRAG_W2 == 1 && FRAG_W2T - FR
                   FRAG_BLOCK_FH - FRAG_W2T == 1, "fragment block layout");
 hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H, int F, hipStream_t s);
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+// Router probability on the FC1 input, every row r < M: out = bf16(p_r x_r)
+// (out may be x); and its input gradient dx = bf16(p_r g_r) (dx may be g),
+// dprobs[r] = sum_h g x (dprobs may be null).  H % 8 == 0.
+hipError_t launch_scale_rows(const uint16_t* x, const float* probs, int64_t M, int H, uint16_t* out,
+                             hipStream_t s);
+hipError_t launch_scale_rows_bwd(const uint16_t* g, const uint16_t* x, const float* probs, int64_t M, int H,
+                                 uint16_t* dx, float* dprobs, hipStream_t s);
 // Device address of the no-allocation scratch array (GG_NOALLOC_SCRATCH_BYTES)
 // on `device`, looked up once per device and cached (gg_noalloc.hip).
 hipError_t noalloc_scratch(int device, void** ptr);

@@ -1945,6 +1945,72 @@ __global__ void round_bf16_kernel(const float* __restrict__ in, uint16_t* __rest
         out[i] = f2bf(in[i]);
 }
 
+// Router probability on the FC1 input (paged-stash pull request, "What does
+// this PR do": the optional multiply by the probability before FC1):
+// out[r][h] = bf16(p_r x[r][h]), the fp32 product rounded to nearest even.
+// One wavefront per row (four per workgroup, rows strided over the grid);
+// lane l takes the row's 16-byte chunks l, l + 64, ...  x and out may be one
+// buffer: a lane reads each chunk before it writes it.
+__global__ __launch_bounds__(256) void scale_rows_kernel(const uint16_t* x, const float* __restrict__ probs,
+                                                         int64_t M, int H, uint16_t* out) {
+    const int lane = threadIdx.x & 63;
+    const int nch = H / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); r < M;
+         r += static_cast<int64_t>(gridDim.x) * 4) {
+        const float p = probs[r];
+        const uint16_t* xr = x + r * H;
+        uint16_t* orow = out + r * H;
+        for (int c = lane; c < nch; c += 64) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xr + c * 8);
+            uint4 o;
+            o.x = pack2(p * lo_f(v.x), p * hi_f(v.x));
+            o.y = pack2(p * lo_f(v.y), p * hi_f(v.y));
+            o.z = pack2(p * lo_f(v.z), p * hi_f(v.z));
+            o.w = pack2(p * lo_f(v.w), p * hi_f(v.w));
+            *reinterpret_cast<uint4*>(orow + c * 8) = o;
+        }
+    }
+}
+
+// Its input gradient, given g (the gradient at the scaled input) and the
+// unscaled x: dx[r][h] = bf16(p_r g[r][h]) and dprobs[r] = sum_h g[r][h] x[r][h]
+// in fp32 (products of two bf16 values are exact).  Lane l adds the products
+// of its chunks l, l + 64, ... in increasing h; the 64 lane sums are then
+// combined pairwise, lanes 32 apart first, so every row's sum has one fixed
+// order.  dx may be g's buffer.
+__global__ __launch_bounds__(256) void scale_rows_bwd_kernel(const uint16_t* g, const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ probs, int64_t M, int H,
+                                                             uint16_t* dx, float* __restrict__ dprobs) {
+    const int lane = threadIdx.x & 63;
+    const int nch = H / 8;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); r < M;
+         r += static_cast<int64_t>(gridDim.x) * 4) {
+        const float p = probs[r];
+        const uint16_t* gr = g + r * H;
+        const uint16_t* xr = x + r * H;
+        uint16_t* drow = dx + r * H;
+        float s = 0.f;
+        for (int c = lane; c < nch; c += 64) {
+            const uint4 gv = *reinterpret_cast<const uint4*>(gr + c * 8);
+            const uint4 xv = *reinterpret_cast<const uint4*>(xr + c * 8);
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            uint32_t ow[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float g0 = lo_f(gw[k]), g1 = hi_f(gw[k]);
+                s += g0 * lo_f(xw[k]);
+                s += g1 * hi_f(xw[k]);
+                ow[k] = pack2(p * g0, p * g1);
+            }
+            *reinterpret_cast<uint4*>(drow + c * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+        if (lane == 0 && dprobs) dprobs[r] = s;
+    }
+}
+
 // dp of every routed row: the partial sums of its 32-column groups added in
 // group order (the same order whichever flavor produced them).
 __global__ void dp_reduce_kernel(const int64_t* __restrict__ offsets, int E, int M, const float* __restrict__ part,
@@ -2039,6 +2105,27 @@ hipError_t launch_dp_reduce(const int64_t* offsets, int E, int M, const float* p
                        ld, dprobs);
     return hipGetLastError();
 }
+namespace {
+unsigned row_blocks(int64_t M) {   // four rows per workgroup, at most 65536 workgroups
+    const int64_t b = (M + 3) / 4;
+    return static_cast<unsigned>(b < 65536 ? b : 65536);
+}
+}  // namespace
+
+hipError_t launch_scale_rows(const uint16_t* x, const float* probs, int64_t M, int H, uint16_t* out,
+                             hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scale_rows_kernel, dim3(row_blocks(M)), dim3(256), 0, s, x, probs, M, H, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_rows_bwd(const uint16_t* g, const uint16_t* x, const float* probs, int64_t M, int H,
+                                 uint16_t* dx, float* dprobs, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scale_rows_bwd_kernel, dim3(row_blocks(M)), dim3(256), 0, s, g, x, probs, M, H, dx, dprobs);
+    return hipGetLastError();
+}
+
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;

@@ -292,6 +292,37 @@ static void test_noalloc() {
     CHECK(g_launches.empty());
 }
 
+static void test_scale_rows() {
+    const int64_t M = 12, H = 40;
+    Buf x(M * H * 2), g(M * H * 2), out(M * H * 2), dx(M * H * 2), pr(M * 4), dp(M * 4);
+    hipStream_t s = fake_stream(0);
+    g_launches.clear();
+    // one launch each, in place allowed, dprobs optional
+    CHECK(gg_scale_rows(x.p, pr.as<float>(), M, H, out.p, s) == GG_OK);
+    CHECK(gg_scale_rows(x.p, pr.as<float>(), M, H, x.p, s) == GG_OK);
+    CHECK(gg_scale_rows_backward(g.p, x.p, pr.as<float>(), M, H, dx.p, dp.as<float>(), s) == GG_OK);
+    CHECK(gg_scale_rows_backward(g.p, x.p, pr.as<float>(), M, H, g.p, nullptr, s) == GG_OK);
+    CHECK(g_launches.size() == 4);
+    if (g_launches.size() == 4) {
+        CHECK(!std::strcmp(g_launches[0].kind, "scale_rows") && g_launches[0].a == M && g_launches[0].b == H);
+        CHECK(!std::strcmp(g_launches[2].kind, "scale_rows_bwd") && g_launches[2].c == 1 && g_launches[3].c == 0);
+    }
+    // argument errors launch nothing; M == 0 needs no pointers
+    g_launches.clear();
+    CHECK(gg_scale_rows(nullptr, nullptr, 0, H, nullptr, s) == GG_OK);
+    CHECK(gg_scale_rows(x.p, pr.as<float>(), M, 36, out.p, s) == GG_ERR_INVALID_ARGUMENT);
+    CHECK(gg_scale_rows(x.p, pr.as<float>(), M, H, x.p + 16, s) == GG_ERR_ALIASING);
+    CHECK(gg_scale_rows(x.p, reinterpret_cast<float*>(pr.p + 2), M, H, out.p, s) == GG_ERR_MISALIGNED);
+    CHECK(gg_scale_rows_backward(g.p, x.p, pr.as<float>(), M, H, x.p, nullptr, s) == GG_ERR_ALIASING);
+    CHECK(gg_scale_rows_backward(g.p, x.p, pr.as<float>(), M, H, dx.p, reinterpret_cast<float*>(dx.p + 64), s) ==
+          GG_ERR_ALIASING);
+    CHECK(g_launches.empty());
+    // the device check applies as to every call
+    fake_set_arch(3, "gfx942");
+    CHECK(gg_scale_rows(x.p, pr.as<float>(), M, H, out.p, fake_stream(3)) == GG_ERR_UNSUPPORTED_DEVICE);
+    CHECK(g_launches.empty());
+}
+
 int main() {
     test_sizes();
     test_argument_checks();
@@ -301,6 +332,7 @@ int main() {
     test_debug_validate();
     test_pack();
     test_noalloc();
+    test_scale_rows();
     std::printf("api_driver: %d of %d checks failed\n", g_failed, g_checked);
     return g_failed == 0 ? 0 : 1;
 }

@@ -31,6 +31,17 @@ hipError_t launch_dp_reduce(const int64_t*, int E, int M, const float*, int ld, 
     g_launches.push_back(l);
     return hipSuccess;
 }
+hipError_t launch_scale_rows(const uint16_t*, const float*, int64_t M, int H, uint16_t*, hipStream_t) {
+    Launch l{"scale_rows", GemmParams{}, 0, nullptr, nullptr, static_cast<int>(M), H, 0};
+    g_launches.push_back(l);
+    return hipSuccess;
+}
+hipError_t launch_scale_rows_bwd(const uint16_t*, const uint16_t*, const float*, int64_t M, int H, uint16_t*,
+                                 float* dprobs, hipStream_t) {
+    Launch l{"scale_rows_bwd", GemmParams{}, 0, nullptr, nullptr, static_cast<int>(M), H, dprobs != nullptr};
+    g_launches.push_back(l);
+    return hipSuccess;
+}
 // The static scratch array of the no-allocation entry point: one host buffer
 // per device here.
 hipError_t noalloc_scratch(int device, void** ptr) {

@@ -233,6 +233,58 @@ def test_glu_entry_points_validate_before_any_hip_call():
     assert L.gg_dgrad_glu(x, h1, off, M, pk, None, 4, H, F, 0, probs, ws, need, dx, probs, None) == ALI
 
 
+def test_scale_rows_entry_points_validate_before_any_hip_call():
+    """Router probability on the FC1 input: shapes, null pointers, alignment
+    and overlaps are refused before any HIP call; in place (x_out == x,
+    dx == dxs) is allowed and so not tried here (it would launch)."""
+    gg = _gg()
+    L = gg.lib
+    INV, MIS, ALI = gg.GG_ERR_INVALID_ARGUMENT, gg.GG_ERR_MISALIGNED, gg.GG_ERR_ALIASING
+    base = 1 << 40
+    M, H = 8, 64                       # 1 KiB per [M][H] bf16 buffer
+    x, pr, out = base, base + 2 ** 30, base + 2 ** 31
+    g, dx, dp = base + 2 ** 32, base + 2 ** 33, base + 2 ** 34
+    # empty batch: nothing to do, no pointers needed
+    assert L.gg_scale_rows(None, None, 0, H, None, None) == 0
+    assert L.gg_scale_rows_backward(None, None, None, 0, H, None, None, None) == 0
+    # shapes
+    assert L.gg_scale_rows(x, pr, M, 12, out, None) == INV
+    assert L.gg_scale_rows(x, pr, M, 0, out, None) == INV
+    assert L.gg_scale_rows(x, pr, -1, H, out, None) == INV
+    assert L.gg_scale_rows_backward(g, x, pr, M, 4, dx, dp, None) == INV
+    # null pointers (dprobs alone may be null)
+    assert L.gg_scale_rows(None, pr, M, H, out, None) == INV
+    assert L.gg_scale_rows(x, None, M, H, out, None) == INV
+    assert L.gg_scale_rows_backward(g, x, None, M, H, dx, dp, None) == INV
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, None, dp, None) == INV
+    # alignment: 16 bytes for the rows, 4 for probs and dprobs
+    assert L.gg_scale_rows(x + 8, pr, M, H, out, None) == MIS
+    assert L.gg_scale_rows(x, pr + 2, M, H, out, None) == MIS
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, dx + 8, dp, None) == MIS
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, dx, dp + 1, None) == MIS
+    # overlaps other than exact in-place use
+    assert L.gg_scale_rows(x, pr, M, H, x + 16, None) == ALI
+    assert L.gg_scale_rows(x, out + 64, M, H, out, None) == ALI
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, g + 16, dp, None) == ALI
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, x, dp, None) == ALI
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, dx, dx + 64, None) == ALI
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, dx, pr, None) == ALI
+    assert L.gg_scale_rows_backward(g, x, pr, M, H, dx, g + 32, None) == ALI
+
+
+def test_scale_rows_binding_checks_before_any_call():
+    gg = _gg()
+    import torch
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    p = torch.ones(4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        gg.gg_scale_rows(x, p)                                   # host tensors
+    with pytest.raises(ValueError):
+        gg.gg_scale_rows(x.float(), p)                           # not bf16
+    with pytest.raises(ValueError):
+        gg.gg_scale_rows_backward(x, x, p)
+
+
 def test_python_binding_refuses_unsupported_weights():
     gg = _gg()
     import torch
