@@ -167,7 +167,10 @@ def parity_of_sample(sample, y_gpu, dx_gpu):
                      "worst_ratio": float(ratio.max()), "over_bound": int((ratio > 1.0).sum()),
                      "elements": int(r.size), "exact_frac": float(np.mean(d == 0))}
     out["rows"] = int(rows.numel())
-    out["bar"] = "rel_l2 <= 2e-3 and |d| <= 1e-2|ref| + 1e-3 per element"
+    out["bar"] = ("end to end, each side from its own forward: rel_l2 <= 2e-3; the per-element bound "
+                  "|d| <= 1e-2|ref| + 1e-3 holds stage by stage (given the same bf16 input of the last "
+                  "rounding) and is counted here, where one-ulp flips of intermediate bf16 values on "
+                  "either side can exceed it")
     return out
 
 
