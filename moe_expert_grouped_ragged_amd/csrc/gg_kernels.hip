@@ -304,6 +304,14 @@ __device__ __forceinline__ int find_expert(const int* s_pre, int E, int t) {
 // that stage from LDS and issues the HBM->LDS copies, and a barrier swaps the
 // roles, so the matrix pipe of every SIMD always has a wave feeding it.
 template <int V> struct GrpTag { static constexpr int value = V; };
+// f(GrpTag<0>{}), ..., f(GrpTag<N - 1>{}): a loop over compile-time indices.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(GrpTag<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 constexpr int TBM = 256, TBN = 256, NWAVES = 8, NTHREADS = NWAVES * 64, NSTAGE = 2;
 constexpr int WROWS = 128, WCOLS = 64, FM = WROWS / 32, FN = WCOLS / 32;
 constexpr int A_STAGE = TBM * BK, B_STAGE = TBN * BK;          // elements per stage
@@ -1441,12 +1449,6 @@ void tile4_kernel(const GemmParams p) {
                 for (int i = 0; i < 3; ++i)
                     tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
             };
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
             // prologue: virtual steps -12..-1; steps -12..-8 issue no weight loads
             // (they come before the first one, so no weight wait counts them).
             // Stage 0's last copy is then followed by 22 loads, not the 24 the
@@ -1461,30 +1463,36 @@ void tile4_kernel(const GemmParams p) {
                 tdma1((g >> 2) + 3, g & 3);
             }
             wait_vmcnt<22>();
-            for (int g0 = 0; g0 < nsteps; g0 += 8) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int g = g0 + u;
-                    const int j4 = u & 3;
-                    if (j4 == 0) {
-                        wait_vmcnt<24>();
-                        block_barrier();
-                        rd3(g, u & 1);
-                    }
-                    if (j4 < 3) rd3(g + 1, (u + 1) & 1);
-                    wfrag_wait19(wr[u][0], wr[u][1]);
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
-                    const int gw = g + 7;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        wfrag_load_m(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j), j ? lm1 : lm0);
-                    tdma1((g >> 2) + 3, j4);
+            // K step g (u = g % 8).  The item's first step starts its sums from
+            // an immediate zero, so the accumulators are never cleared.
+            auto kstep = [&](int g, auto u_tag, auto first_tag) {
+                constexpr int u = decltype(u_tag)::value;
+                constexpr int j4 = u & 3;
+                if constexpr (j4 == 0) {
+                    wait_vmcnt<24>();
+                    block_barrier();
+                    rd3(g, u & 1);
                 }
-            }
+                if constexpr (j4 < 3) rd3(g + 1, (u + 1) & 1);
+                wfrag_wait19(wr[u][0], wr[u][1]);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if constexpr (decltype(first_tag)::value != 0)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], f32x16{}, 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
+                    }
+                const int gw = g + 7;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    wfrag_load_m(wr[(u + 7) & 7][j], wp(gw < nsteps ? gw : nsteps - 1, j), j ? lm1 : lm0);
+                tdma1((g >> 2) + 3, j4);
+            };
+            static_for<8>([&](auto ut) { kstep(decltype(ut)::value, ut, GrpTag<(decltype(ut)::value == 0)>{}); });
+            for (int g0 = 8; g0 < nsteps; g0 += 8)
+                static_for<8>([&](auto ut) { kstep(g0 + decltype(ut)::value, ut, GrpTag<0>{}); });
             wait_vmcnt<0>();
 #pragma unroll
             for (int s = 0; s < 8; ++s) wfrag_hold2(wr[s][0], wr[s][1]);
@@ -1655,12 +1663,6 @@ void tile4_kernel(const GemmParams p) {
                 for (int i = 0; i < 8; ++i)
                     tf[buf][i] = *reinterpret_cast<const bf16x8*>(st + kc_off(i * 32 + (lane & 31), ch));
             };
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
             // prologue: virtual steps -13..-1 (weights of steps 0..6 from step -7
             // on, token stages 0..2 and the first copy of stage 3); step -1 ends
             // like the last step of a stage: stage 0 is in, and its first step's
@@ -1681,39 +1683,45 @@ void tile4_kernel(const GemmParams p) {
                 }
                 tdma(((g + 1) >> 2) + 3, (g + 1) & 3);
             }
-            for (int g0 = 0; g0 < nsteps; g0 += 8) {
+            // K step g (u = g % 8).  The tile's first step starts its sums from
+            // an immediate zero, so the accumulators are never cleared.
+            auto kstep = [&](int g, auto u_tag, auto first_tag) {
+                constexpr int u = decltype(u_tag)::value;
+                constexpr int j4 = u & 3;
+                // this step's weights; in a stage's last step also this wave's
+                // copies of the next stage (28 loads were issued after them)
+                wfrag_wait26(wr[u][0], wr[u][1]);
+                // In a stage's last step: every wave's copies of the next
+                // stage are in, and every wave has read all of this stage's
+                // fragments, so its slot may be refilled from here on.
+                if constexpr (j4 == 3) block_barrier();
+                rd_t(g + 1, (u + 1) & 1);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int g = g0 + u;
-                    const int j4 = u & 3;
-                    // this step's weights; in a stage's last step also this wave's
-                    // copies of the next stage (28 loads were issued after them)
-                    wfrag_wait26(wr[u][0], wr[u][1]);
-                    // In a stage's last step: every wave's copies of the next
-                    // stage are in, and every wave has read all of this stage's
-                    // fragments, so its slot may be refilled from here on.
-                    if (j4 == 3) block_barrier();
-                    rd_t(g + 1, (u + 1) & 1);
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < 2; ++j) {
+                        if constexpr (decltype(first_tag)::value != 0)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], f32x16{}, 0, 0, 0);
+                        else
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], tf[u & 1][i], acc[i][j], 0, 0, 0);
-                    const int gw = g + 7;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
-                    tdma(((g + 1) >> 2) + 3, (j4 + 1) & 3);
-                    // issue order within the step: one token fragment read for the
-                    // next step after each of the first eight MFMAs, so the reads
-                    // spread over the step instead of bunching behind its MFMAs
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                const int gw = g + 7;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) wfrag_load(wr[(u + 7) & 7][j], wptr(gw < nsteps ? gw : nsteps - 1, j));
+                tdma(((g + 1) >> 2) + 3, (j4 + 1) & 3);
+                // issue order within the step: one token fragment read for the
+                // next step after each of the first eight MFMAs, so the reads
+                // spread over the step instead of bunching behind its MFMAs
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 }
-            }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            };
+            static_for<8>([&](auto ut) { kstep(decltype(ut)::value, ut, GrpTag<(decltype(ut)::value == 0)>{}); });
+            for (int g0 = 8; g0 < nsteps; g0 += 8)
+                static_for<8>([&](auto ut) { kstep(g0 + decltype(ut)::value, ut, GrpTag<0>{}); });
             // drain the clamped loads; the ring becomes the epilogue's staging area
             wait_vmcnt<0>();
 #pragma unroll
