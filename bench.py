@@ -42,6 +42,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,10 +61,17 @@ KERNEL_SOURCES = ["moe_expert_grouped_ragged_amd/csrc/gg_kernels.hip",
 
 
 def kernel_source_hash() -> str:
+    """sha256 (16 hex digits) of the kernel and launch sources with their
+    comments removed and whitespace collapsed, so that a measurement keyed by
+    it goes stale when the code changes but not when only a comment or the
+    layout does (the sources hold no string literal with a comment marker)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1244,9 +1244,11 @@ void grouped_gemm_kernel(const GemmParams p) {
 // ---------------------------------------------------------------- four-wave kernel
 //
 // The four GEMMs over the caller's fragment-ordered copy of the weights (an
-// optional buffer, for H % 256 == 0 and F % 128 == 0), each in one launch:
-// first thin items (the at most 96 rows an expert leaves after its 256-row
-// tiles, or all rows of a small expert), then the tiles.  Four waves compute
+// optional buffer, for H % 256 == 0 and F % 128 == 0), each in one launch
+// over a work list of thin items (the at most 96 rows an expert leaves after
+// its 256-row tiles, or all rows of a small expert), then tiles; workgroups
+// of even XCDs run their thin items first, those of odd XCDs their tiles
+// first.  Four waves compute
 // a 256 x 256 tile: wave w owns all 256 token rows and its own 64 weight rows
 // (two 32-row blocks), as 8 x 2 accumulator blocks of 32 x 32 (all 256
 // AGPRs), so that no two waves load the same weight bytes.  Tokens stream
