@@ -1384,7 +1384,7 @@ void tile4_kernel(const GemmParams p) {
     bf16x8 wr[8][2];
     bf16x8 tf[2][8];
 
-    // ---- thin items first: rows x TILE_COLS output columns.  Each wave owns
+    // ---- thin items: rows x TILE_COLS output columns.  Each wave owns
     // two 32-row weight blocks (for SwiGLU the gate and up rows of 32
     // features) against three 32-row token blocks.  Per k16 step: two weight
     // loads seven steps ahead and one of the four token copies of the stage
@@ -1614,7 +1614,7 @@ void tile4_kernel(const GemmParams p) {
             block_barrier();   // staging reads done before the next copies land
         }
 
-        // ---- then the 256-row tiles.  Wave w owns all 256 token rows and its own
+        // ---- the 256-row tiles.  Wave w owns all 256 token rows and its own
         // 64 weight rows (two 32-row blocks: for SwiGLU the gate and up rows of 32
         // features, else 64 output columns), as 8 x 2 accumulator blocks of
         // 32 x 32 (all 256 AGPRs).  So no two waves load the same weight bytes:
