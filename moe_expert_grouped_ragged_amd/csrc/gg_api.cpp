@@ -406,7 +406,7 @@ int dgrad_impl(const void* dy, const void* h1, const void* x, const int64_t* off
                             : nullptr;
     p.dp_part = dp_part;
     p.dp_ld = static_cast<int>(dp_groups(F));
-    p.wfrag = frag_matrix(frag, gg::FRAG_W2T, H, F);   // W2^T fragments (four-wave tiles, plain SwiGLU)
+    p.wfrag = frag_matrix(frag, gg::FRAG_W2T, H, F);   // W2^T fragments (four-wave tiles, F % 256 == 0)
     if (gg::launch_dgrad_fc2(p, info.num_cu, stream) != hipSuccess) return GG_ERR_HIP;
     if (dprobs && gg::launch_dp_reduce(offsets, static_cast<int>(E), static_cast<int>(M), dp_part,
                                        static_cast<int>(dp_groups(F)), dprobs, stream) != hipSuccess)

@@ -1326,11 +1326,16 @@ __device__ __forceinline__ void wfrag_wait26(bf16x8& a, bf16x8& b) {
     asm volatile("s_waitcnt vmcnt(26)" : "+v"(a), "+v"(b) :: "memory");
 }
 
-// The plain SwiGLU derivative of four consecutive features of one token row,
+// The activation derivative of four consecutive features of one token row,
 // in place: g, u are the saved bf16 gate and up values at pg and pu, the
 // results dG, dU overwrite them; dA = bf16(a[4q + x]).  The same arithmetic,
-// in the same order, as the eight-wave kernel's derivative epilogues.
-__device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, const f32x16& a, int q) {
+// in the same order, as the eight-wave kernel's derivative epilogues: plain
+// SwiGLU without EXT; with EXT the sigmoid slope, the row's probability pr
+// (when weighted) and the row's dp partial sum dps, which gains the four
+// features' da * act(g) * u in increasing x.
+template <bool EXT>
+__device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, const f32x16& a, int q, float slope,
+                                                float pr, bool weighted, float& dps) {
     const uint2 hg = *reinterpret_cast<const uint2*>(pg);
     const uint2 hu = *reinterpret_cast<const uint2*>(pu);
     const uint32_t gw[2] = {hg.x, hg.y};
@@ -1342,9 +1347,17 @@ __device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, cons
         const float g = (x & 1) ? hi_f(gw[x >> 1]) : lo_f(gw[x >> 1]);
         const float u = (x & 1) ? hi_f(uw[x >> 1]) : lo_f(uw[x >> 1]);
         const float da = (x & 1) ? hi_f(dw[x >> 1]) : lo_f(dw[x >> 1]);
-        const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(1.0f * g)));
-        dg[x] = da * u * sgm * (1.0f + 1.0f * g * (1.0f - sgm));
-        du[x] = da * g * sgm;
+        if constexpr (EXT) {
+            const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(slope * g)));
+            const float dap = weighted ? pr * da : da;
+            dg[x] = dap * u * sgm * (1.0f + slope * g * (1.0f - sgm));
+            du[x] = dap * g * sgm;
+            dps += da * (g * sgm * u);
+        } else {
+            const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-(1.0f * g)));
+            dg[x] = da * u * sgm * (1.0f + 1.0f * g * (1.0f - sgm));
+            du[x] = da * g * sgm;
+        }
     }
     *reinterpret_cast<uint2*>(pg) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
     *reinterpret_cast<uint2*>(pu) = make_uint2(pack2(du[0], du[1]), pack2(du[2], du[3]));
@@ -1353,8 +1366,8 @@ __device__ __forceinline__ void dswiglu_inplace(uint16_t* pg, uint16_t* pu, cons
 template <int EPI, bool EXT>
 __global__ __launch_bounds__(T4_THREADS, 1)
 void tile4_kernel(const GemmParams p) {
-    static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU || (EPI == EPI_DSWIGLU && !EXT),
-                  "store, SwiGLU, and the plain SwiGLU derivative");
+    static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU,
+                  "store, SwiGLU and the activation derivative");
     const float slope = EXT ? p.slope : 1.0f;
     const float* const probs = EXT ? p.probs : nullptr;
     __shared__ __attribute__((aligned(1024))) uint16_t s_ring[T4_NSLOT * T4_SLOT];
@@ -1554,14 +1567,23 @@ void tile4_kernel(const GemmParams p) {
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
                     const int r = i * 32 + (ln & 31);
+                    const float pr = (probs && r < rows) ? probs[trow0 + r] : 1.0f;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
+                    for (int j = 0; j < 2; ++j) {
+                        float dps = 0.0f;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int pos = (4 * j + q) ^ (r & 7);
                             uint16_t* pg = stg + r * 128 + pos * 8 + 4 * (ln >> 5);
-                            dswiglu_inplace(pg, pg + 64, acc[i][j], q);
+                            dswiglu_inplace<EXT>(pg, pg + 64, acc[i][j], q, slope, pr, probs != nullptr, dps);
                         }
+                        if (EXT && p.dp_part) {
+                            // the 32 features' partial sum, in the eight-wave kernel's order
+                            const float tot = dps + __shfl_xor(dps, 32, 64);
+                            if (ln < 32 && r < rows)
+                                p.dp_part[static_cast<int64_t>(trow0 + r) * p.dp_ld + (f0 + 32 * j) / 32] = tot;
+                        }
+                    }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 4
@@ -1841,14 +1863,25 @@ void tile4_kernel(const GemmParams p) {
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int r = ii * 32 + (ln & 31);
+                        const int prow = trow0 + pass * 64 + r;
+                        const float pr = (probs && prow < row_end) ? probs[prow] : 1.0f;
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
+                        for (int j = 0; j < 2; ++j) {
+                            float dps = 0.0f;
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
                                 const int pos = (4 * j + q) ^ (r & 7);
                                 uint16_t* pg = bb + r * 128 + pos * 8 + 4 * (ln >> 5);
-                                dswiglu_inplace(pg, pg + 64, acc[2 * pass + ii][j], q);
+                                dswiglu_inplace<EXT>(pg, pg + 64, acc[2 * pass + ii][j], q, slope, pr,
+                                                     probs != nullptr, dps);
                             }
+                            if (EXT && p.dp_part) {
+                                // the 32 features' partial sum, in the eight-wave kernel's order
+                                const float tot = dps + __shfl_xor(dps, 32, 64);
+                                if (ln < 32 && prow < row_end)
+                                    p.dp_part[static_cast<int64_t>(prow) * p.dp_ld + (f0 + 32 * j) / 32] = tot;
+                            }
+                        }
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 };
@@ -2098,7 +2131,9 @@ hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H
 // weighted and QuickGeGLU variants, and every other shape, on the eight-wave
 // kernel (the same bits either way).
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
-    if (p.wfrag && plain_swiglu(p) && p.N % TBN == 0) return launch_tile4<EPI_DSWIGLU, false>(p, num_cu, s);
+    if (p.wfrag && p.N % TBN == 0)
+        return plain_swiglu(p) ? launch_tile4<EPI_DSWIGLU, false>(p, num_cu, s)
+                               : launch_tile4<EPI_DSWIGLU, true>(p, num_cu, s);
     return plain_swiglu(p) ? launch_cfg<true, EPI_DSWIGLU, false>(p, num_cu, s)
                            : launch_cfg<true, EPI_DSWIGLU, true>(p, num_cu, s);
 }

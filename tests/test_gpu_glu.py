@@ -49,7 +49,8 @@ def _run(c, act, probs_np, want_dprobs=True, frag=False):
 
 @pytest.mark.parametrize("act", ["swiglu", "qgeglu"])
 @pytest.mark.parametrize("counts,H,F,frag", [case + (False,) for case in CASES] +
-                         [([300, 0, 257, 40, 1, 97], 256, 128, True)])   # four-wave forward tiles and dX
+                         [([300, 0, 257, 40, 1, 97], 256, 128, True),    # four-wave forward tiles and dX
+                          ([300, 0, 257, 40, 1, 97], 256, 256, True)])   # and dA (F % 256 == 0)
 def test_glu_stagewise_parity(act, counts, H, F, frag):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -59,6 +60,24 @@ def test_glu_stagewise_parity(act, counts, H, F, frag):
     h1, a, y, dh1, dx, dprobs = _run(c, act, probs, frag=frag)
     infos = stagewise_glu(c.x, c.dy, c.offsets, c.w1, c.w2, act, probs, h1, a, y, dh1, dx, dprobs)
     log("  " + " ".join(f"{i['name']}:{i.get('rel_l2', 0):.1e}" for i in infos))
+
+
+@pytest.mark.parametrize("act,weighted", [("qgeglu", True), ("swiglu", True), ("qgeglu", False)])
+def test_fragment_buffer_gives_the_same_bits(act, weighted):
+    """With F % 256 == 0 the four-wave kernel also runs dA with the
+    activation options (slope, row probabilities, dp partial sums); every
+    output, dprobs included, equals the run without the fragment buffer (the
+    eight-wave kernel) bit for bit: thin items, partial and full tiles."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = workload.custom_case([300, 0, 257, 40, 1, 97, 512], 256, 256, seed=47)
+    probs = _probs(c.M, 9) if weighted else None
+    log(f"[glu] fragment buffer vs packed act={act} weighted={weighted}")
+    ref = _run(c, act, probs, frag=False)
+    got = _run(c, act, probs, frag=True)
+    for name, g, r in zip(("h1", "a", "y", "dh1", "dx"), got[:5], ref[:5]):
+        assert torch.equal(g.view(torch.int16), r.view(torch.int16)), name
+    assert torch.equal(got[5], ref[5]), "dprobs"
 
 
 def test_unit_probs_and_no_probs_are_bitwise_the_plain_path():
