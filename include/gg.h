@@ -193,8 +193,8 @@ int gg_forward_fc2_frag(const void* a, const int64_t* offsets, int64_t M,
  * the partial sums).  Two launches on `stream`, three with dprobs.  With
  * GG_ACT_SWIGLU, probs == NULL and dprobs == NULL the results are those of
  * gg_dgrad, bit for bit.  `frag` as in gg_forward_fc1_glu (used by the dX
- * GEMM, and by dA with F % 256 == 0; the results do not
- * depend on it). */
+ * GEMM, and by dA when F % 256 == 0, for every activation and with or
+ * without probs; the results, dprobs included, do not depend on it). */
 int gg_dgrad_glu(const void* dy, const void* h1, const int64_t* offsets, int64_t M,
                  const void* packed, const void* frag, int64_t E, int64_t H, int64_t F,
                  int activation, const float* probs,
