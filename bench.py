@@ -323,6 +323,9 @@ def main():
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
 
+    if args.weighted and args.probs_on_input:
+        print("bench.py: --weighted and --probs-on-input are alternatives", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU only (no sharding or collectives are part of it); "
               "use --gpus 1", file=sys.stderr)
@@ -371,9 +374,6 @@ def main():
     y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     dx = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
-    if args.weighted and args.probs_on_input:
-        print("bench.py: --weighted and --probs-on-input are alternatives", file=sys.stderr)
-        sys.exit(2)
     glu = args.activation != "swiglu" or args.weighted or args.recompute
     with_probs = args.weighted or args.probs_on_input
     probs_np = (np.random.default_rng(w.seed + 17).uniform(0.05, 1.0, M).astype(np.float32)

@@ -13,6 +13,13 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in proc.stderr
 
 
+def test_weighted_and_probs_on_input_are_alternatives():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--weighted", "--probs-on-input"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "alternatives" in proc.stderr
+
+
 def test_cpu_baseline_on_the_tiny_workload():
     sys.path.insert(0, ROOT)
     import bench
