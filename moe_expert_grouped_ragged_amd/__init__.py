@@ -61,7 +61,8 @@ ACTIVATIONS = {"swiglu": GG_ACT_SWIGLU, "qgeglu": GG_ACT_QGEGLU}
 EXPORTED = ("gg_status_string", "gg_packed_bytes", "gg_dgrad_workspace_bytes", "gg_pack_weights",
             "gg_forward_fc1_swiglu", "gg_forward_fc2", "gg_dgrad", "gg_round_bf16",
             "gg_dgrad_glu_workspace_bytes", "gg_forward_fc1_glu", "gg_dgrad_glu", "gg_dgrad_recompute",
-            "gg_frag_bytes", "gg_pack_frag", "gg_forward_fc2_frag", "gg_dgrad_noalloc")
+            "gg_frag_bytes", "gg_pack_frag", "gg_forward_fc2_frag", "gg_dgrad_noalloc",
+            "gg_scale_rows", "gg_scale_rows_backward")
 
 
 def _load() -> ctypes.CDLL:
@@ -141,10 +142,11 @@ def _bf16_cuda(t: torch.Tensor, name: str, shape=None, device=None) -> torch.Ten
 
 
 def _offsets(offsets: torch.Tensor, E: int, device) -> torch.Tensor:
+    """The split offsets as given (no copy: a strided tensor is refused)."""
     if (not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.int64 or not offsets.is_cuda
-            or offsets.shape != (E + 1,) or offsets.device != device):
-        raise ValueError(f"offsets must be an int64 tensor of shape [E+1] on {device}")
-    return offsets.contiguous()
+            or offsets.shape != (E + 1,) or offsets.device != device or not offsets.is_contiguous()):
+        raise ValueError(f"offsets must be a contiguous int64 tensor of shape [E+1] on {device}")
+    return offsets
 
 
 def _packed(packed: torch.Tensor, E: int, H: int, F: int, device) -> torch.Tensor:

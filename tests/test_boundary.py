@@ -37,6 +37,10 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", gg.LIB_PATH], capture_output=True, text=True)
     exported = set(re.findall(r"\bT (gg_[a-z0-9_]+)", out.stdout))
     assert set(declared_functions()) <= exported
+    # the binding gives every declared function its C signature
+    assert set(gg.EXPORTED) == set(declared_functions())
+    for n in gg.EXPORTED:
+        assert getattr(gg.lib, n).argtypes is not None, n
 
 
 def test_header_compiles_as_c():
@@ -143,6 +147,9 @@ def test_python_binding_checks_buffers_before_any_call():
         gg.gg_dgrad(fake((M, H)), fake((M, 2 * F)), off, packed, E, H, F, workspace=fake((M, F)))
     with pytest.raises(ValueError, match="offsets must be"):
         gg.gg_forward_fc2(fake((M, F)), fake((E,), torch.int64), packed, E, H, F)
+    with pytest.raises(ValueError, match="offsets must be a contiguous"):
+        gg.gg_dgrad_noalloc(fake((M, H)), fake((M, 2 * F)), fake((2 * E + 2,), torch.int64)[::2], packed,
+                            E, H, F)
     with pytest.raises(ValueError, match="no fragment-ordered copies"):
         gg.gg_forward_fc2_frag(fake((M, F)), off, packed, fake((1024,)), E, H, F)
     E2, H2, F2 = 2, 256, 128
