@@ -23,7 +23,10 @@
  *
  * Conventions shared by every call
  *  - Tensors are DEVICE pointers to bf16 bit patterns, row-major, 16-byte
- *    aligned.  `offsets` is a DEVICE pointer to E+1 int64 values.
+ *    aligned.  `offsets` is a DEVICE pointer to E+1 int64 values.  Every
+ *    buffer of a call lies on the stream's device (the current device for
+ *    the null stream), where the call's kernels run; the library does not
+ *    look up which device a pointer belongs to.
  *  - Rows are sorted by expert: expert e owns rows [offsets[e], offsets[e+1]).
  *    offsets must be non-decreasing with 0 <= offsets[0] and offsets[E] <= M.
  *    An expert with offsets[e] == offsets[e+1] has no tokens: nothing is read

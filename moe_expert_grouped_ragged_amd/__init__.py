@@ -115,9 +115,15 @@ def _check(status: int, what: str) -> None:
         raise GGError(status, what)
 
 
-def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return int(s.cuda_stream)
+def _stream_ptr(stream: Optional[torch.cuda.Stream], device: torch.device) -> int:
+    """The given stream, or the current stream of the tensors' device; the
+    library runs on the stream's device, so a stream of another device is
+    refused."""
+    if stream is None:
+        return int(torch.cuda.current_stream(device).cuda_stream)
+    if stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+    return int(stream.cuda_stream)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -240,7 +246,7 @@ def gg_pack_weights(w1: Union[torch.Tensor, Sequence[torch.Tensor]],
     arr1 = (ctypes.c_void_p * E)(*[t.data_ptr() for t in w1s])
     arr2 = (ctypes.c_void_p * E)(*[t.data_ptr() for t in w2s])
     _check(lib.gg_pack_weights(E, H, F, arr1, arr2, packed.data_ptr(), packed.numel() * 2,
-                               _stream_ptr(stream)), "gg_pack_weights")
+                               _stream_ptr(stream, w1s[0].device)), "gg_pack_weights")
     return packed
 
 
@@ -257,7 +263,7 @@ def gg_pack_frag(packed: torch.Tensor, E: int, H: int, F: int, frag: Optional[to
         frag = torch.empty(need // 2, dtype=torch.bfloat16, device=packed.device)
     _frag(frag, E, H, F, packed.device)
     _check(lib.gg_pack_frag(E, H, F, packed.data_ptr(), packed.numel() * 2, frag.data_ptr(), frag.numel() * 2,
-                            _stream_ptr(stream)), "gg_pack_frag")
+                            _stream_ptr(stream, packed.device)), "gg_pack_frag")
     return frag
 
 
@@ -288,7 +294,7 @@ def gg_forward_fc1_swiglu(x: torch.Tensor, offsets: torch.Tensor, packed: torch.
     if h1_out is None and save_h1:
         h1_out = _out(None, (M, 2 * F), "h1_out", dev)
     _check(lib.gg_forward_fc1_swiglu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
-                                     _ptr(h1_out), a_out.data_ptr(), _stream_ptr(stream)),
+                                     _ptr(h1_out), a_out.data_ptr(), _stream_ptr(stream, dev)),
            "gg_forward_fc1_swiglu")
     return h1_out, a_out
 
@@ -313,11 +319,11 @@ def gg_forward_fc2_frag(a: torch.Tensor, offsets: torch.Tensor, packed: torch.Te
     y = _out(y, (M, H), "y", dev)
     if fr is None:
         st = lib.gg_forward_fc2(a.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F, y.data_ptr(),
-                                _stream_ptr(stream))
+                                _stream_ptr(stream, dev))
         _check(st, "gg_forward_fc2")
     else:
         st = lib.gg_forward_fc2_frag(a.data_ptr(), off.data_ptr(), M, packed.data_ptr(), fr.data_ptr(), E, H, F,
-                                     y.data_ptr(), _stream_ptr(stream))
+                                     y.data_ptr(), _stream_ptr(stream, dev))
         _check(st, "gg_forward_fc2_frag")
     return y
 
@@ -343,7 +349,7 @@ def gg_dgrad(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, packed: 
     dx = _out(dx, (M, H), "dx", dev)
     _check(lib.gg_dgrad(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                        dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad")
+                        dx.data_ptr(), _stream_ptr(stream, dev)), "gg_dgrad")
     return dx
 
 
@@ -364,7 +370,7 @@ def gg_dgrad_noalloc(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, 
     off = _offsets(offsets, E, dev)
     dx = _out(dx, (M, H), "dx", dev)
     _check(lib.gg_dgrad_noalloc(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), E, H, F,
-                                dx.data_ptr(), _stream_ptr(stream)), "gg_dgrad_noalloc")
+                                dx.data_ptr(), _stream_ptr(stream, dev)), "gg_dgrad_noalloc")
     return dx
 
 
@@ -412,7 +418,7 @@ def gg_forward_fc1_glu(x: torch.Tensor, offsets: torch.Tensor, packed: torch.Ten
         h1_out = _out(None, (M, 2 * F), "h1_out", dev)
     _check(lib.gg_forward_fc1_glu(x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr), E, H, F,
                                   _activation(activation), _ptr(pr), _ptr(h1_out), a_out.data_ptr(),
-                                  _stream_ptr(stream)), "gg_forward_fc1_glu")
+                                  _stream_ptr(stream, dev)), "gg_forward_fc1_glu")
     return h1_out, a_out
 
 
@@ -446,7 +452,7 @@ def gg_dgrad_glu(dy: torch.Tensor, h1: torch.Tensor, offsets: torch.Tensor, pack
     _check(lib.gg_dgrad_glu(dy.data_ptr(), h1.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr), E, H, F,
                             _activation(activation), _ptr(pr), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
-                            _stream_ptr(stream)), "gg_dgrad_glu")
+                            _stream_ptr(stream, dev)), "gg_dgrad_glu")
     return dx, dprobs
 
 
@@ -480,7 +486,7 @@ def gg_dgrad_recompute(dy: torch.Tensor, x: torch.Tensor, offsets: torch.Tensor,
     _check(lib.gg_dgrad_recompute(dy.data_ptr(), x.data_ptr(), off.data_ptr(), M, packed.data_ptr(), _ptr(fr),
                                   E, H, F, _activation(activation), _ptr(pr), workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), dx.data_ptr(), _ptr(dprobs),
-                                  _stream_ptr(stream)), "gg_dgrad_recompute")
+                                  _stream_ptr(stream, dev)), "gg_dgrad_recompute")
     return dx, dprobs
 
 
@@ -489,7 +495,7 @@ def gg_round_bf16(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 device tensor")
     out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
-    _check(lib.gg_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream_ptr(stream)),
+    _check(lib.gg_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream_ptr(stream, x.device)),
            "gg_round_bf16")
     return out
 
@@ -506,7 +512,7 @@ def gg_scale_rows(x: torch.Tensor, probs: torch.Tensor, out: Optional[torch.Tens
     if pr is None:
         raise ValueError("probs is required")
     out = _out(out, (M, H), "out", x.device)
-    _check(lib.gg_scale_rows(x.data_ptr(), pr.data_ptr(), M, H, out.data_ptr(), _stream_ptr(stream)),
+    _check(lib.gg_scale_rows(x.data_ptr(), pr.data_ptr(), M, H, out.data_ptr(), _stream_ptr(stream, x.device)),
            "gg_scale_rows")
     return out
 
@@ -530,7 +536,7 @@ def gg_scale_rows_backward(dxs: torch.Tensor, x: torch.Tensor, probs: torch.Tens
     if dprobs is None and want_dprobs:
         dprobs = torch.empty(M, dtype=torch.float32, device=dxs.device)
     _check(lib.gg_scale_rows_backward(dxs.data_ptr(), x.data_ptr(), pr.data_ptr(), M, H, dx.data_ptr(),
-                                      _ptr(dprobs), _stream_ptr(stream)), "gg_scale_rows_backward")
+                                      _ptr(dprobs), _stream_ptr(stream, dxs.device)), "gg_scale_rows_backward")
     return dx, dprobs
 
 
