@@ -33,8 +33,8 @@ struct GemmParams {
                                // 32-column group [M][dp_ld], or null
     int dp_ld;                 // ceil(N / 32)
     // This GEMM's matrix in the caller's fragment-ordered copy of the weights,
-    // or null.  With it, the GEMM runs in the four-wave kernel (dgrad FC2: the
-    // plain SwiGLU derivative with F a multiple of 256).
+    // or null.  With it, the GEMM runs in the four-wave kernel (dgrad FC2: F a
+    // multiple of 256).
     const uint16_t* wfrag;
     int64_t wfrag_stride;      // elements between consecutive experts in the fragment copy
     int h1_order;              // plain store over W1's fragment copy: write the columns in H1's gate | up order

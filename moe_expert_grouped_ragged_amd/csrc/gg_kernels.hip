@@ -2126,9 +2126,9 @@ hipError_t launch_pack_frag(const uint16_t* packed, uint16_t* frag, int E, int H
                        F);
     return hipGetLastError();
 }
-// The plain SwiGLU derivative runs on four-wave tiles over W2^T's fragment
-// copy when there is one and F is a multiple of the 256-column tile; the
-// weighted and QuickGeGLU variants, and every other shape, on the eight-wave
+// The SwiGLU derivative (plain, or with the slope, the row weights and dp)
+// runs on four-wave tiles over W2^T's fragment copy when there is one and F
+// is a multiple of the 256-column tile; every other shape on the eight-wave
 // kernel (the same bits either way).
 hipError_t launch_dgrad_fc2(const GemmParams& p, int num_cu, hipStream_t s) {
     if (p.wfrag && p.N % TBN == 0)

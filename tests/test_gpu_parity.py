@@ -341,6 +341,35 @@ def test_padded_workload_every_tile():
     _full_size_run("padded_e128_h4096_f2048", whole=False)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("H,F", [(256, 128), (16384, 32640)])
+def test_largest_expert_matrix(H, F):
+    """The largest expert matrices the boundary accepts: at H = 16384,
+    F = 32640 one expert's W1 is 4FH = 2,139,095,040 bytes, just under the
+    2^31-byte limit, so the kernels' 32-bit byte offsets inside a matrix and
+    a token panel reach their largest values, and the second expert's
+    weights start 3.2 GB into the packed buffer.  Expert 0 has 40 rows (a
+    thin item only), expert 1 has 300 (a full tile and a thin remainder).
+    Both weight layouts run the whole problem with NaN-filled outputs; the
+    oracle computes the first and last rows of each expert and both sides of
+    the tile boundary, every stage."""
+    _gpu_ok()
+    log(f"[max] drawing E=2 H={H} F={F}")
+    case = workload.custom_case([40, 300], H, F, seed=31)
+    dc, (h1, a, y, ws, dx) = run_layouts(case, canary=True)
+    for name, t in (("h1", h1), ("a", a), ("y", y), ("dh1", ws), ("dx", dx)):
+        assert bool(torch.isfinite(t).all()), f"{name}: an element was never written"
+    rows = np.array([0, 39, 40, 41, 295, 296, 297, 339], dtype=np.int64)
+    _, compact = oracle.sample_rows(case.offsets, rows)
+    rt = torch.from_numpy(rows)
+    rd = rt.to(dc.dev)
+    log(f"[max] oracle on rows {rows.tolist()}")
+    w1f, w2f = oracle._as_f32(case.w1), oracle._as_f32(case.w2)
+    out = stagewise(case.x[rt], case.dy[rt], compact, w1f, w2f, h1[rd], a[rd], y[rd], ws[rd], dx[rd],
+                    exact=False)
+    log(f"[max] H={H} F={F} ok: " + summary(out))
+
+
 def test_fragment_ordered_copies_layout():
     """The opt-in fragment buffer: per expert, W1 (rows in feature blocks of 64,
     gate rows then up rows), W2, W1^T and W2^T, each in blocks of 32 rows x 16 k
