@@ -135,13 +135,24 @@ def test_dprobs_rows_outside_offsets_untouched_and_empty_batch():
 def test_glu_workload_sampled_rows(wl):
     """Full-size workloads in the benchmark's launch configuration; the oracle
     checks a sample of rows from both flavors (every row depends only on its
-    own inputs and its expert's weights)."""
+    own inputs and its expert's weights).  Where the shape has fragment
+    copies, the run with them (four-wave tiles for all four GEMMs, dA with
+    the slope, the row weights and dp) equals the run without them bit for
+    bit over every output, dprobs included."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    import moe_expert_grouped_ragged_amd as gg
     c = workload.draw_case(workload.by_name(wl))
     probs = _probs(c.M, 11)
     log(f"[glu] workload {wl} M={c.M}")
     h1, a, y, dh1, dx, dprobs = _run(c, "qgeglu", probs)
+    if gg.has_frag(c.H, c.F):
+        got = _run(c, "qgeglu", probs, frag=True)
+        for name, g, r in zip(("h1", "a", "y", "dh1", "dx", "dprobs"), got, (h1, a, y, dh1, dx, dprobs)):
+            assert torch.equal(g.view(torch.int32) if g.dtype == torch.float32 else g.view(torch.int16),
+                               r.view(torch.int32) if r.dtype == torch.float32 else r.view(torch.int16)), name
+        log(f"[glu] workload {wl}: with fragment copies, bitwise equal")
+        del got
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([rng.choice(c.M, 96, replace=False),
                                      c.offsets[1:-1][np.diff(c.offsets)[1:] > 0][:16]]))
