@@ -9,8 +9,8 @@
 //
 // Two kernels.  The eight-wave kernel (grouped_gemm_kernel) runs every GEMM
 // over the row-major packed weights; the four-wave kernel (tile4_kernel,
-// below) runs FC1, FC2, dX and, for plain SwiGLU, the dgrad FC2 when the
-// caller also passes a fragment-ordered copy of the weights.  In the
+// below) runs FC1, FC2, dX and, with F a multiple of 256, the dgrad FC2 when
+// the caller also passes a fragment-ordered copy of the weights.  In the
 // eight-wave kernel two flavors share one launch.  Rows that fill 256-row
 // tiles run as 256 x 256 output tiles; the at most 96 rows an expert leaves
 // over (all rows of a small expert) run as weight-streaming items, before the
