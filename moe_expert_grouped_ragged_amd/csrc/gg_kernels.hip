@@ -1248,10 +1248,10 @@ void grouped_gemm_kernel(const GemmParams p) {
 // over a work list of thin items (the at most 96 rows an expert leaves after
 // its 256-row tiles, or all rows of a small expert), then tiles; workgroups
 // of even XCDs run their thin items first, those of odd XCDs their tiles
-// first.  Four waves compute
-// a 256 x 256 tile: wave w owns all 256 token rows and its own 64 weight rows
-// (two 32-row blocks), as 8 x 2 accumulator blocks of 32 x 32 (all 256
-// AGPRs), so that no two waves load the same weight bytes.  Tokens stream
+// first.  Four waves compute a 256 x 256 tile: wave w owns all 256 token
+// rows and its own 64 weight rows (two 32-row blocks), as 8 x 2 accumulator
+// blocks of 32 x 32 (all 256 AGPRs), so that no two waves load the same
+// weight bytes.  Tokens stream
 // through a 4-slot LDS ring of 64-k stages by LDS-DMA, three stages ahead,
 // and each wave reads a step's eight token fragments from it.  Weights skip
 // LDS: in the fragment-ordered copy the 64 lanes' 16-byte operands of one
@@ -1268,9 +1268,9 @@ void grouped_gemm_kernel(const GemmParams p) {
 // before step 0 repeat the pattern as the prologue (without the weight loads
 // that would come before the first real one, which no wait counts), and the
 // steps past the end re-load clamped addresses, so the counts hold
-// everywhere.  The sums are
-// the same MFMA chain over k as in the eight-wave tiles and the streaming
-// items, so a row's results do not depend on which flavor computed it.
+// everywhere.  The sums are the same MFMA chain over k as in the eight-wave
+// tiles and the streaming items, so a row's results do not depend on which
+// flavor computed it.
 //
 // Fragment order: block b of 32 weight rows and k16 step s of an expert is
 // 512 contiguous elements; lane l's 8 are rows 32b + (l & 31), k 16s + 8(l >> 5).
@@ -1303,9 +1303,6 @@ __device__ __forceinline__ void wfrag_load_m(bf16x8& w, const uint16_t* ptr, uin
                  : "memory");
 }
 #pragma clang diagnostic pop
-// Waits for the weight fragments of the current step (at most N loads issued
-// after them may be outstanding) tie the registers they guard, so that nothing
-// reads them before the wait.
 // H1 = X W1^T over the fragment-ordered W1 (plain-store variant): the copy's
 // 32-row block b holds W1 rows gate/up of 32 features (gate, gate, up, up per
 // 64 features), so its outputs go to H1 column h1_col(b, F) onwards.
@@ -1313,10 +1310,14 @@ __device__ __forceinline__ int h1_col(int b, int F) {
     return ((b & 3) < 2 ? 0 : F) + (b >> 2) * 64 + (b & 1) * 32;
 }
 __device__ __forceinline__ int F_of(int N) { return N >> 1; }   // N = 2F for the H1 GEMM
-// The same for a thin item's step (two weight blocks, 19 later loads).
+// Waits for the weight fragments of the current step (at most N loads issued
+// after them may be outstanding) tie the registers they guard, so that nothing
+// reads them before the wait.  A thin item's step: two weight blocks, 19
+// later loads.
 __device__ __forceinline__ void wfrag_wait19(bf16x8& a, bf16x8& b) {
     asm volatile("s_waitcnt vmcnt(19)" : "+v"(a), "+v"(b) :: "memory");
 }
+// Ties two registers without a wait (after a wait that covers them).
 __device__ __forceinline__ void wfrag_hold2(bf16x8& a, bf16x8& b) {
     asm volatile("" : "+v"(a), "+v"(b) :: "memory");
 }
